@@ -1,0 +1,338 @@
+/*
+ * CPU oracle for the sparse Mixture-of-Experts layer forward pass.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no code,
+ * header, table or helper with the HIP library in
+ * sparse_mixture_experts_gating_amd/; it is written from the pages, plainly,
+ * in double precision, with no blocking, fusion or reordering.  OpenMP only
+ * spreads independent outputs over threads; every output is summed in the
+ * same order whatever the thread count.
+ *
+ * Pages cited (titles as published):
+ *   [devtips]  devtips.kr, "MoE (Mixture of Experts) 아키텍처 완전 정복:
+ *              Mixtral부터 DeepSeek-MoE까지 구현 원리와 실전 최적화 기법"
+ *   [garden]   ricepunchb.github.io obsidian garden, "Mixture of Experts (MoE)"
+ *   [yj-zh]    youngju.dev, "Mixture of Experts（MoE）架构深度解析：从 Switch
+ *              Transformer 到 Mixtral 的演进与高效扩展策略"
+ *   [yj-ja]    youngju.dev, "Sparse Mixture of Experts（MoE）アーキテクチャ深層分析：
+ *              設計原理からDeepSeek-V3・Qwen3まで"
+ *   [lecture]  study-site lecture-03, "Mixture of Experts"
+ *
+ * Conventions shared with the tests (not with the GPU code):
+ *   - all float inputs arrive as float32 arrays; bf16 workloads pass their
+ *     bf16-rounded values, which float32 holds exactly;
+ *   - weights follow nn.Linear: [out][in], stacked over experts;
+ *   - intermediate expert outputs stay in double; only final results are
+ *     rounded (by the caller) to float32.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define GATE_TOPK_SOFTMAX 0 /* top-k on logits, softmax over the k kept */
+#define GATE_SOFTMAX_TOPK 1 /* softmax over all experts, zero outside top-k */
+#define GATE_SWITCH 2       /* top-1, gate = largest softmax probability */
+
+#define ACT_RELU 0
+#define ACT_GELU_ERF 1
+#define ACT_SWIGLU 2
+
+/* Selection order used everywhere: a larger logit ranks first; equal logits
+ * rank the lower index first.  The pages use torch.topk, whose order among
+ * equal values is unspecified; lowest-index-first is the reading taken.
+ * IEEE comparison already treats -0.0 and +0.0 as equal. */
+static int ranks_before(float a, int64_t ia, float b, int64_t ib) {
+    if (a > b) return 1;
+    if (a < b) return 0;
+    return ia < ib;
+}
+
+/* Router logits: l[t][e] = sum_i x[t][i] * Wg[e][i] + b[e], summed in double
+ * and rounded once to float32.  [devtips] MoELayer (gate = nn.Linear with
+ * bias); [yj-zh] GatingNetwork / MixtralMoELayer (bias-free gate); [yj-ja]
+ * gating formula "W_g * x". */
+void oracle_logits(int64_t T, int32_t d, int32_t E, const float *x,
+                   const float *wg, const float *bias, float *logits) {
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t e = 0; e < E; ++e) {
+            double s = 0.0;
+            for (int32_t i = 0; i < d; ++i)
+                s += (double)x[t * d + i] * (double)wg[(int64_t)e * d + i];
+            if (bias) s += (double)bias[e];
+            logits[t * E + e] = (float)s;
+        }
+    }
+}
+
+/* Token-choice gating for every token.
+ * Selection: the k experts that rank first (slot j holds rank j), picked by
+ * k plain scans.  Weights by mode:
+ *   GATE_TOPK_SOFTMAX: softmax over the k selected logits -- [devtips]
+ *     MoELayer.forward, [yj-zh] GatingNetwork and MixtralMoELayer.  Softmax
+ *     over all experts followed by renormalising the k kept probabilities
+ *     ([yj-ja] TopKGating) gives the same numbers in exact arithmetic.
+ *   GATE_SOFTMAX_TOPK: softmax over all E logits, kept as is for the
+ *     selected experts (the [yj-ja] gating formula, no renormalisation).
+ *   GATE_SWITCH (k == 1): the largest softmax probability over all E
+ *     ([yj-zh] SwitchRouter: probs.max).
+ * Returns 0, or -1 on bad arguments. */
+int oracle_route_topk(int64_t T, int32_t E, int32_t k, int32_t mode,
+                      const float *logits, int32_t *idx, float *w) {
+    if (k < 1 || k > E) return -1;
+    if (mode == GATE_SWITCH && k != 1) return -1;
+    if (mode < 0 || mode > 2) return -1;
+    int bad = 0;
+#pragma omp parallel
+    {
+        unsigned char *taken = (unsigned char *)malloc((size_t)E);
+        if (!taken) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(static)
+            for (int64_t t = 0; t < T; ++t) {
+                const float *l = logits + t * E;
+                memset(taken, 0, (size_t)E);
+                for (int32_t j = 0; j < k; ++j) {
+                    int32_t best = -1;
+                    for (int32_t e = 0; e < E; ++e) {
+                        if (taken[e]) continue;
+                        if (best < 0 || ranks_before(l[e], e, l[best], best)) best = e;
+                    }
+                    taken[best] = 1;
+                    idx[t * k + j] = best;
+                }
+                double top = (double)l[idx[t * k]];
+                if (mode == GATE_TOPK_SOFTMAX) {
+                    double z = 0.0;
+                    for (int32_t j = 0; j < k; ++j) z += exp((double)l[idx[t * k + j]] - top);
+                    for (int32_t j = 0; j < k; ++j)
+                        w[t * k + j] = (float)(exp((double)l[idx[t * k + j]] - top) / z);
+                } else {
+                    /* the top-ranked logit is the maximum over all experts */
+                    double z = 0.0;
+                    for (int32_t e = 0; e < E; ++e) z += exp((double)l[e] - top);
+                    for (int32_t j = 0; j < k; ++j)
+                        w[t * k + j] = (float)(exp((double)l[idx[t * k + j]] - top) / z);
+                }
+            }
+            free(taken);
+        }
+    }
+    return bad ? -1 : 0;
+}
+
+/* Capacity as the pages compute it: int(capacity_factor * tokens / experts),
+ * truncated toward zero ([yj-zh] SwitchRouter and ExpertChoiceRouter;
+ * [yj-ja] ExpertChoiceGating).  Evaluated in double. */
+int32_t oracle_capacity(double capacity_factor, int64_t tokens, int32_t E) {
+    return (int32_t)(capacity_factor * (double)tokens / (double)E);
+}
+
+/* Counts, capacity and the expert-contiguous permutation (token choice).
+ *   keep rule: with capacity > 0, tokens are split into consecutive groups of
+ *     `group` tokens (group <= 0: one group of all T).  Inside a group the
+ *     assignments are visited token by token, slot by slot; an assignment to
+ *     expert e is kept while fewer than `capacity` assignments of that group
+ *     have been kept for e, and dropped after ([yj-zh] SwitchRouter keeps the
+ *     first `capacity` positions of each expert and clears the rest).
+ *   counts[e]  = kept assignments of expert e; offsets = exclusive prefix sum
+ *     ([yj-ja] compute_load_balancing_loss counts tokens per expert).
+ *   rows: expert e owns rows offsets[e] .. offsets[e+1]-1 and lists its tokens
+ *     in ascending token order, the order x[mask] yields in [yj-zh] MoELayer.
+ *   row_token[r] = token of row r; slot_row[t*k+j] = row of assignment (t,j),
+ *     or -1 when it was dropped.
+ * Returns the number of kept assignments, or -1 on bad arguments. */
+int64_t oracle_permute(int64_t T, int32_t E, int32_t k, const int32_t *idx,
+                       int32_t capacity, int64_t group, int32_t *counts,
+                       int32_t *offsets, int32_t *row_token, int32_t *slot_row) {
+    if (k < 1 || E < 1) return -1;
+    for (int64_t a = 0; a < T * k; ++a)
+        if (idx[a] < 0 || idx[a] >= E) return -1;
+    unsigned char *kept = (unsigned char *)malloc((size_t)(T * k > 0 ? T * k : 1));
+    int32_t *used = (int32_t *)calloc((size_t)E, sizeof(int32_t));
+    if (!kept || !used) { free(kept); free(used); return -1; }
+    int64_t G = (group > 0) ? group : (T > 0 ? T : 1);
+    for (int64_t t = 0; t < T; ++t) {
+        if (t % G == 0) memset(used, 0, (size_t)E * sizeof(int32_t));
+        for (int32_t j = 0; j < k; ++j) {
+            int32_t e = idx[t * k + j];
+            if (capacity <= 0 || used[e] < capacity) {
+                kept[t * k + j] = 1;
+                used[e] += 1;
+            } else {
+                kept[t * k + j] = 0;
+            }
+        }
+    }
+    for (int32_t e = 0; e < E; ++e) counts[e] = 0;
+    for (int64_t a = 0; a < T * k; ++a)
+        if (kept[a]) counts[idx[a]] += 1;
+    offsets[0] = 0;
+    for (int32_t e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+    for (int32_t e = 0; e < E; ++e) used[e] = offsets[e];
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t j = 0; j < k; ++j) {
+            if (!kept[t * k + j]) { slot_row[t * k + j] = -1; continue; }
+            int32_t e = idx[t * k + j];
+            int32_t r = used[e]++;
+            row_token[r] = (int32_t)t;
+            slot_row[t * k + j] = r;
+        }
+    }
+    int64_t total = offsets[E];
+    free(kept);
+    free(used);
+    return total;
+}
+
+/* Expert-choice routing ([yj-zh] ExpertChoiceRouter; [yj-ja]
+ * ExpertChoiceGating): each expert scores every token with a softmax taken
+ * over the token axis of the logits, then keeps its C best tokens.
+ * Selection ranks tokens by logit (larger first, lower token first on
+ * equal logits); softmax over tokens is monotone in the logit, so this is
+ * the same order as ranking by score.  ec_idx[e][j] lists the chosen tokens
+ * in that rank order; ec_score[e][j] is the chosen token's score. */
+int oracle_route_expert_choice(int64_t T, int32_t E, int32_t C,
+                               const float *logits, int32_t *ec_idx,
+                               float *ec_score) {
+    if (C < 1 || C > T) return -1;
+    int bad = 0;
+#pragma omp parallel
+    {
+        unsigned char *taken = (unsigned char *)malloc((size_t)T);
+        if (!taken) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(static)
+            for (int32_t e = 0; e < E; ++e) {
+                double m = -INFINITY;
+                for (int64_t t = 0; t < T; ++t)
+                    if ((double)logits[t * E + e] > m) m = (double)logits[t * E + e];
+                double z = 0.0;
+                for (int64_t t = 0; t < T; ++t) z += exp((double)logits[t * E + e] - m);
+                memset(taken, 0, (size_t)T);
+                for (int32_t j = 0; j < C; ++j) {
+                    int64_t best = -1;
+                    for (int64_t t = 0; t < T; ++t) {
+                        if (taken[t]) continue;
+                        if (best < 0 || ranks_before(logits[t * E + e], t, logits[best * E + e], best))
+                            best = t;
+                    }
+                    taken[best] = 1;
+                    ec_idx[(int64_t)e * C + j] = (int32_t)best;
+                    ec_score[(int64_t)e * C + j] =
+                        (float)(exp((double)logits[best * E + e] - m) / z);
+                }
+            }
+            free(taken);
+        }
+    }
+    return bad ? -1 : 0;
+}
+
+static double act_relu(double z) { return z > 0.0 ? z : 0.0; }
+/* GELU in its exact erf form, the default of nn.GELU ([yj-zh] MoELayer). */
+static double act_gelu(double z) { return 0.5 * z * (1.0 + erf(z / sqrt(2.0))); }
+/* SiLU(z) = z * sigmoid(z) ([lecture] SiLU / SwiGLU / MoE table). */
+static double act_silu(double z) { return z / (1.0 + exp(-z)); }
+
+/* One expert's FFN on `nrows` input rows X[r][0..d).
+ *   ACT_RELU / ACT_GELU_ERF: y = W2 act(W1 u + b1) + b2  ([devtips] MoELayer
+ *     experts: Linear, ReLU, Linear with biases; [yj-zh] MoELayer experts:
+ *     Linear, GELU, Linear).  b1/b2 may be NULL.
+ *   ACT_SWIGLU: y = W2 (silu(W1 u) * (W3 u))  ([yj-zh] SwiGLUExpert with
+ *     w1 = gate, w3 = up, w2 = down; [yj-ja] SwiGLUExpert w_gate / w_up /
+ *     w_down, dropout off at inference; [lecture] table row for SwiGLU).
+ * w1, w3: [F][d]; w2: [d][F]; Y: [nrows][d] in double. */
+int oracle_expert_ffn(int32_t act, int32_t d, int32_t F, int64_t nrows,
+                      const float *X, const float *w1, const float *w3,
+                      const float *w2, const float *b1, const float *b2,
+                      double *Y) {
+    if (act < 0 || act > 2) return -1;
+    if (act == ACT_SWIGLU && !w3) return -1;
+    int bad = 0;
+#pragma omp parallel
+    {
+        double *h = (double *)malloc((size_t)F * sizeof(double));
+        if (!h) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t r = 0; r < nrows; ++r) {
+                const float *u = X + r * d;
+                for (int32_t f = 0; f < F; ++f) {
+                    double a = 0.0;
+                    for (int32_t i = 0; i < d; ++i) a += (double)w1[(int64_t)f * d + i] * (double)u[i];
+                    if (act == ACT_SWIGLU) {
+                        double b = 0.0;
+                        for (int32_t i = 0; i < d; ++i) b += (double)w3[(int64_t)f * d + i] * (double)u[i];
+                        h[f] = act_silu(a) * b;
+                    } else {
+                        if (b1) a += (double)b1[f];
+                        h[f] = (act == ACT_RELU) ? act_relu(a) : act_gelu(a);
+                    }
+                }
+                for (int32_t o = 0; o < d; ++o) {
+                    double s = 0.0;
+                    for (int32_t f = 0; f < F; ++f) s += (double)w2[(int64_t)o * F + f] * h[f];
+                    if (act != ACT_SWIGLU && b2) s += (double)b2[o];
+                    Y[r * d + o] = s;
+                }
+            }
+            free(h);
+        }
+    }
+    return bad ? -1 : 0;
+}
+
+/* Gate-weighted sum for token choice: y[t] = sum over kept slots j, in slot
+ * order, of w[t][j] * Y[slot_row[t][j]], plus the always-on shared expert's
+ * output Ys[t] when given (gate weight 1).  A token whose slots were all
+ * dropped gets 0 plus the shared term.  [yj-ja] gating formula
+ * y = sum_i G(x)_i E_i(x); [devtips] / [yj-zh] output[mask] += w * out;
+ * [yj-zh] DeepSeekMoELayer shared_out + routed_out. */
+void oracle_combine_topk(int64_t T, int32_t k, int32_t d, const float *w,
+                         const int32_t *slot_row, const double *Y,
+                         const double *Ys, double *y) {
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t o = 0; o < d; ++o) y[t * d + o] = 0.0;
+        for (int32_t j = 0; j < k; ++j) {
+            int32_t r = slot_row[t * k + j];
+            if (r < 0) continue;
+            double g = (double)w[t * k + j];
+            for (int32_t o = 0; o < d; ++o) y[t * d + o] += g * Y[(int64_t)r * d + o];
+        }
+        if (Ys)
+            for (int32_t o = 0; o < d; ++o) y[t * d + o] += Ys[t * d + o];
+    }
+}
+
+/* Gate-weighted sum for expert choice: the dispatch matrix D[e][t] holds the
+ * score where expert e chose token t and 0 elsewhere ([yj-ja]
+ * ExpertChoiceGating scatters the scores into it), so
+ * y[t] = sum_e D[e][t] * E_e(x_t), summed over e ascending.  Row e*C + j of Y
+ * is expert e's output for its j-th chosen token.  Tokens no expert chose
+ * get 0 (plus Ys[t] when given). */
+void oracle_combine_expert_choice(int64_t T, int32_t E, int32_t C, int32_t d,
+                                  const int32_t *ec_idx, const float *ec_score,
+                                  const double *Y, const double *Ys, double *y) {
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t o = 0; o < d; ++o) y[t * d + o] = Ys ? Ys[t * d + o] : 0.0;
+        for (int32_t e = 0; e < E; ++e) {
+            for (int32_t j = 0; j < C; ++j) {
+                if (ec_idx[(int64_t)e * C + j] != t) continue;
+                double g = (double)ec_score[(int64_t)e * C + j];
+                const double *row = Y + ((int64_t)e * C + j) * d;
+                for (int32_t o = 0; o < d; ++o) y[t * d + o] += g * row[o];
+            }
+        }
+    }
+}
