@@ -1,0 +1,93 @@
+// Gate-weighted combine on gfx950: y[t] = sum over slots of w * y_perm[row]
+// (+ shared expert output), the mixture y = sum_i G(x)_i E_i(x) of [yj-ja]
+// youngju.dev "Sparse Mixture of Experts（MoE）アーキテクチャ深層分析" (gating
+// formula), gathered per token instead of scattered with atomics, so the sum
+// runs in a fixed order (slot order; expert order for expert choice) and is
+// deterministic.  One wave per token, eight elements per lane per step.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+template <typename T>
+__device__ inline void load8(const T *p, float *v);
+template <>
+__device__ inline void load8<bf16>(const bf16 *p, float *v) {
+    const bf16x8 b = __builtin_bit_cast(bf16x8, load16(p));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (float)b[i];
+}
+template <>
+__device__ inline void load8<float>(const float *p, float *v) {
+    const u32x4 a = load16(p), b = load16(p + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[i] = __uint_as_float(a[i]);
+        v[4 + i] = __uint_as_float(b[i]);
+    }
+}
+template <typename T>
+__device__ inline void store8(T *p, const float *v);
+template <>
+__device__ inline void store8<bf16>(bf16 *p, const float *v) {
+    bf16x8 b;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) b[i] = (bf16)v[i];
+    store16(p, __builtin_bit_cast(u32x4, b));
+}
+template <>
+__device__ inline void store8<float>(float *p, const float *v) {
+    u32x4 a, b;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        a[i] = __float_as_uint(v[i]);
+        b[i] = __float_as_uint(v[4 + i]);
+    }
+    store16(p, a);
+    store16(p + 4, b);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void combine_kernel(const T *__restrict__ y_perm, const T *__restrict__ y_shared,
+                                                      const float *__restrict__ w,
+                                                      const int32_t *__restrict__ slot_row, int Tn, int d, int S,
+                                                      int expert_choice, T *__restrict__ y) {
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+    if (t >= Tn) return;
+    const int32_t *sr = slot_row + t * S;
+    for (int c0 = lane * 8; c0 < d; c0 += kWave * 8) {
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < S; ++s) {
+            const int row = sr[s];
+            if (row < 0) continue;
+            const float g = expert_choice ? w[row] : w[t * S + s];
+            float v[8];
+            load8<T>(y_perm + (int64_t)row * d + c0, v);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] = fmaf(g, v[i], acc[i]);
+        }
+        if (y_shared) {
+            float v[8];
+            load8<T>(y_shared + t * d + c0, v);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] += v[i];
+        }
+        store8<T>(y + t * d + c0, acc);
+    }
+}
+
+void launch_combine(const CombineArgs &a, hipStream_t s) {
+    if (a.T == 0) return;
+    const dim3 grid((a.T + 3) / 4);
+    if (a.bf16)
+        hipLaunchKernelGGL(combine_kernel<bf16>, grid, dim3(256), 0, s, (const bf16 *)a.y_perm,
+                           (const bf16 *)a.y_shared, a.w, a.slot_row, a.T, a.d, a.S, (int)a.expert_choice,
+                           (bf16 *)a.y);
+    else
+        hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, s, (const float *)a.y_perm,
+                           (const float *)a.y_shared, a.w, a.slot_row, a.T, a.d, a.S, (int)a.expert_choice,
+                           (float *)a.y);
+}
+
+}  // namespace moe

@@ -1,0 +1,85 @@
+// Shared device helpers for the gfx950 kernels of the MoE layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace moe {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// Element types the kernels are instantiated for.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+    __device__ static inline float load(const float *p) { return *p; }
+    __device__ static inline void store(float *p, float v) { *p = v; }
+};
+template <> struct Elem<bf16> {
+    __device__ static inline float load(const bf16 *p) { return (float)(*p); }
+    // float -> bf16 rounds to nearest even (v_cvt_pk_bf16_f32 on gfx950)
+    __device__ static inline void store(bf16 *p, float v) { *p = (bf16)v; }
+};
+
+__device__ inline u32x4 load16(const void *p) { return *(const u32x4 *)p; }
+__device__ inline void store16(void *p, u32x4 v) { *(u32x4 *)p = v; }
+
+// Order-preserving unsigned image of a float32: a > b  <=>  key(a) > key(b),
+// with -0.0 mapped to the image of +0.0 so that the two tie.
+__device__ inline uint32_t order_key(float v) {
+    uint32_t u = __float_as_uint(v);
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ inline float key_value(uint32_t k) {
+    uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+    return __uint_as_float(u);
+}
+// Unique rank key: larger value first, then lower index first.
+__device__ inline uint64_t rank_key(float v, uint32_t idx) {
+    return ((uint64_t)order_key(v) << 32) | (uint64_t)(~idx);
+}
+__device__ inline uint32_t rank_key_index(uint64_t key) { return ~(uint32_t)(key & 0xffffffffu); }
+
+__device__ inline uint64_t shfl_xor_u64(uint64_t v, int mask) {
+    uint32_t lo = __shfl_xor((uint32_t)v, mask, kWave);
+    uint32_t hi = __shfl_xor((uint32_t)(v >> 32), mask, kWave);
+    return ((uint64_t)hi << 32) | lo;
+}
+__device__ inline uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        uint64_t o = shfl_xor_u64(v, m);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+// Butterfly sum: every lane ends with the same value, in a fixed order.
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+    return v;
+}
+__device__ inline float wave_max(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
+    return v;
+}
+
+__device__ inline float silu(float z) { return z / (1.0f + expf(-z)); }
+__device__ inline float gelu_erf(float z) { return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f)); }
+
+__device__ inline float apply_act(int act, float z) {
+    if (act == kActRelu) return z > 0.f ? z : 0.f;
+    if (act == kActGelu) return gelu_erf(z);
+    return z;
+}
+
+}  // namespace moe

@@ -1,0 +1,85 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+enum ActKind { kActRelu = 0, kActGelu = 1, kActSwiglu = 2, kActNone = 3 };
+enum GateKind { kGateTopkSoftmax = 0, kGateSoftmaxTopk = 1, kGateSwitch = 2, kGateExpertChoice = 3 };
+
+constexpr int kEcMaxCapacity = 4096;  // LDS sort buffer of the expert-choice select
+constexpr int kChunk = 64;            // tokens per permutation chunk (one wave)
+
+// ---- route ----
+struct RouteArgs {
+    const void *x;
+    const void *wg;
+    const float *bias;
+    int T, d, E, k, gating;
+    bool bf16;
+    float *logits;  // may be null for token choice
+    int32_t *idx;
+    float *w;
+};
+void launch_route(const RouteArgs &a, hipStream_t s);
+void launch_gate_logits(const float *logits, int T, int E, int k, int gating, int32_t *idx, float *w,
+                        hipStream_t s);
+void launch_ec_select(const float *logits, int T, int E, int C, int32_t *ec_idx, float *ec_score,
+                      hipStream_t s);
+
+// ---- permute ----
+struct PermuteArgs {
+    const int32_t *idx;  // [T][k]
+    int T, E, k;
+    int capacity;        // 0 = none
+    int group_chunks;    // chunks per capacity group (0 = all)
+    int32_t *chunk_counts, *chunk_pre, *chunk_base;  // [NC][E]
+    int32_t *ranks;      // [T][k]
+    int32_t *counts, *offsets, *row_token, *slot_row;
+};
+void launch_permute_count(const PermuteArgs &a, hipStream_t s);
+void launch_permute_scan(const PermuteArgs &a, hipStream_t s);
+void launch_permute_scatter(const PermuteArgs &a, hipStream_t s);
+void launch_ec_permute(const int32_t *ec_idx, int T, int E, int C, int32_t *counts, int32_t *offsets,
+                       int32_t *row_token, int32_t *slot_row, hipStream_t s);
+void launch_gather_rows(const void *x, const int32_t *row_token, const int32_t *offsets, int E, int64_t rows_max,
+                        int d, int elem_bytes, void *x_perm, hipStream_t s);
+
+// ---- expert FFN ----
+// Tile plan: mstart[e] = sum over experts e' < e of ceil(counts[e'] / BM), mstart[E] = total.
+void launch_tile_plan(const int32_t *counts, int E, int BM, int32_t *mstart, hipStream_t s);
+
+struct GemmArgs {
+    const void *A;          // [rows][K] dtype (row r of group g at offsets[g] + i)
+    const void *B0;         // [G][N][K] (SwiGLU: gate projection)
+    const void *B1;         // [G][N][K] up projection (SwiGLU) or null
+    const float *bias;      // [G][N] or null
+    void *C;                // [rows][N] dtype
+    const int32_t *offsets; // [G+1] or null: one group of `rows` rows
+    const int32_t *mstart;  // [G+1] tile plan for the kernel's BM, or null with offsets null
+    int G;                  // groups (experts)
+    int64_t rows;           // rows of the single group when offsets is null; else A_max (grid bound)
+    int N, K;
+    int act;                // ActKind; kActSwiglu uses B1
+    bool bf16;
+};
+enum GemmShape { kGemmPrefill = 0, kGemmSmallM = 1, kGemmDecode = 2 };
+int gemm_block_m(int shape, bool bf16);
+void launch_grouped_gemm(const GemmArgs &a, int shape, hipStream_t s);
+
+// ---- combine ----
+struct CombineArgs {
+    const void *y_perm;    // [A_max][d]
+    const void *y_shared;  // [T][d] or null
+    const float *w;        // token choice: [T][k]; expert choice: [E*C] scores by row
+    const int32_t *slot_row;  // [T][S]
+    int T, d, S;           // S = k (token choice) or E (expert choice)
+    bool expert_choice;
+    bool bf16;
+    void *y;               // [T][d]
+};
+void launch_combine(const CombineArgs &a, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,371 @@
+// Router GEMM fused with wave-level gating, gating on given logits, and
+// expert-choice selection, for gfx950.
+//
+// Pages (titles as published):
+//   [devtips] devtips.kr "MoE (Mixture of Experts) 아키텍처 완전 정복" -- MoELayer
+//   [yj-zh]   youngju.dev "Mixture of Experts（MoE）架构深度解析" -- GatingNetwork,
+//             SwitchRouter, MixtralMoELayer, ExpertChoiceRouter
+//   [yj-ja]   youngju.dev "Sparse Mixture of Experts（MoE）アーキテクチャ深層分析" --
+//             gating formula, TopKGating, ExpertChoiceGating
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+// One wave gates one token whose E float32 logits start at `row`.
+// Lane l holds experts l, l+64, l+128, l+192 (E <= 256).  Selection repeats a
+// wave-wide maximum of unique rank keys (value desc, index asc) k times, so
+// the slots come out in rank order.  Weights:
+//   topk-softmax: softmax over the k selected logits ([yj-zh] GatingNetwork);
+//   softmax-topk / switch: softmax over all E logits taken at the selected
+//   experts ([yj-ja] gating formula; [yj-zh] SwitchRouter probs.max).
+__device__ void gate_one_token(const float *row, int E, int k, int gating, int64_t t,
+                               int32_t *__restrict__ idx_out, float *__restrict__ w_out) {
+    const int lane = threadIdx.x % kWave;
+    uint64_t key[4];
+    float val[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int e = lane + kWave * q;
+        if (e < E) {
+            val[q] = row[e];
+            key[q] = rank_key(val[q], (uint32_t)e);
+        } else {
+            val[q] = 0.f;
+            key[q] = 0ull;  // below every finite key
+        }
+    }
+    int32_t sel_idx[4] = {0, 0, 0, 0};
+    float sel_val[4] = {0.f, 0.f, 0.f, 0.f};
+    float top = 0.f;
+    for (int j = 0; j < k; ++j) {
+        uint64_t m = key[0];
+#pragma unroll
+        for (int q = 1; q < 4; ++q) m = key[q] > m ? key[q] : m;
+        m = wave_max_u64(m);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (key[q] == m) key[q] = 0ull;
+        const float v = key_value((uint32_t)(m >> 32));
+        if (j == 0) top = v;
+        if (lane == (j & (kWave - 1))) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if ((j >> 6) == q) {
+                    sel_idx[q] = (int32_t)rank_key_index(m);
+                    sel_val[q] = v;
+                }
+        }
+    }
+    float part = 0.f;
+    if (gating == kGateTopkSoftmax) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (lane + kWave * q < k) part += expf(sel_val[q] - top);
+    } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (lane + kWave * q < E) part += expf(val[q] - top);
+    }
+    const float z = wave_sum(part);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int j = lane + kWave * q;
+        if (j < k) {
+            idx_out[t * k + j] = sel_idx[q];
+            w_out[t * k + j] = expf(sel_val[q] - top) / z;
+        }
+    }
+}
+
+// Router GEMM on bf16 MFMA (v_mfma_f32_16x16x32_bf16) + gating epilogue.
+// A block owns 16*WM tokens; its 4 waves form WM (tokens) x WK (K split)
+// with WM*WK = 4.  Each wave computes 16 tokens x 16*NT experts over its K
+// range, straight from global memory (x rows are read once; the router
+// weights stay in L1/L2).  Partial sums meet in LDS in a fixed order, the
+// bias is added, logits are written, and each wave gates whole tokens.
+template <int WM, int NT>
+__global__ __launch_bounds__(256) void route_bf16_kernel(
+    const bf16 *__restrict__ x, const bf16 *__restrict__ wg, const float *__restrict__ bias,
+    int T, int d, int E, int k, int gating, float *__restrict__ logits,
+    int32_t *__restrict__ idx_out, float *__restrict__ w_out) {
+    constexpr int WK = 4 / WM;
+    constexpr int TOK = 16 * WM;
+    constexpr int EP = 16 * NT;
+    constexpr int LD = EP + 4;
+    __shared__ float part[WK * TOK * LD];
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int wm = wave % WM, wk = wave / WM;
+    const int64_t tok0 = (int64_t)blockIdx.x * TOK;
+    const int r = lane % 16, kq = (lane / 16) * 8;
+    int64_t trow = tok0 + wm * 16 + r;
+    if (trow >= T) trow = T - 1;
+    const bf16 *xa = x + trow * d + kq;
+    const bf16 *wb[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        int e = nt * 16 + r;
+        if (e >= E) e = E - 1;
+        wb[nt] = wg + (int64_t)e * d + kq;
+    }
+    f32x4 acc[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int nk = d / 32;
+    const int kb = nk * wk / WK, ke = nk * (wk + 1) / WK;
+    for (int kc = kb; kc < ke; ++kc) {
+        const bf16x8 a = __builtin_bit_cast(bf16x8, load16(xa + kc * 32));
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const bf16x8 b = __builtin_bit_cast(bf16x8, load16(wb[nt] + kc * 32));
+            acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[nt], 0, 0, 0);
+        }
+    }
+    // D[row = 4*(lane/16) + j][col = lane%16] of each 16x16 tile
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            part[(wk * TOK + wm * 16 + 4 * (lane / 16) + j) * LD + nt * 16 + r] = acc[nt][j];
+    __syncthreads();
+    for (int i = threadIdx.x; i < TOK * EP; i += 256) {
+        const int tt = i / EP, e = i % EP;
+        float s = part[tt * LD + e];
+#pragma unroll
+        for (int w = 1; w < WK; ++w) s += part[(w * TOK + tt) * LD + e];
+        if (e < E) {
+            if (bias) s += bias[e];
+            if (logits && tok0 + tt < T) logits[(tok0 + tt) * E + e] = s;
+        }
+        part[tt * LD + e] = s;
+    }
+    __syncthreads();
+    if (gating == kGateExpertChoice) return;
+    for (int tt = wave; tt < TOK; tt += 4) {
+        const int64_t t = tok0 + tt;
+        if (t < T) gate_one_token(part + tt * LD, E, k, gating, t, idx_out, w_out);
+    }
+}
+
+// float32 router (VALU): one wave per token, lane per expert, plus gating.
+__global__ __launch_bounds__(256) void route_f32_kernel(
+    const float *__restrict__ x, const float *__restrict__ wg, const float *__restrict__ bias,
+    int T, int d, int E, int k, int gating, float *__restrict__ logits,
+    int32_t *__restrict__ idx_out, float *__restrict__ w_out) {
+    __shared__ float rows[4][256];
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+    const bool live = t < T;
+    if (live) {
+        for (int e = lane; e < E; e += kWave) {
+            const float *xr = x + t * d;
+            const float *wr = wg + (int64_t)e * d;
+            float s = 0.f;
+            for (int i = 0; i < d; ++i) s = fmaf(xr[i], wr[i], s);
+            if (bias) s += bias[e];
+            rows[wave][e] = s;
+            if (logits) logits[t * E + e] = s;
+        }
+    }
+    __syncthreads();
+    if (live && gating != kGateExpertChoice) gate_one_token(rows[wave], E, k, gating, t, idx_out, w_out);
+}
+
+// Gating alone on given float32 logits [T][E]: one wave per token.
+__global__ __launch_bounds__(256) void gate_logits_kernel(const float *__restrict__ logits, int T, int E,
+                                                           int k, int gating, int32_t *__restrict__ idx_out,
+                                                           float *__restrict__ w_out) {
+    const int wave = threadIdx.x / kWave;
+    const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+    if (t < T) gate_one_token(logits + t * E, E, k, gating, t, idx_out, w_out);
+}
+
+// ---------------------------------------------------------------------------
+// Expert choice ([yj-zh] ExpertChoiceRouter; [yj-ja] ExpertChoiceGating):
+// block e scores every token with softmax over the token axis of column e
+// and keeps the C best tokens by (logit desc, token asc).
+//   1. column max m and sum z of exp(l - m) (fixed-order block reductions);
+//   2. radix select (4 x 8-bit digits of the order key) of the C-th key;
+//   3. ordered compaction: keys above the threshold, then the lowest-index
+//      tokens equal to it until C are taken;
+//   4. bitonic sort of the C unique 64-bit rank keys in LDS, descending;
+//   5. write tokens and scores exp(l - m) / z in rank order.
+// ---------------------------------------------------------------------------
+constexpr int kEcThreads = 1024;
+
+__device__ inline float block_reduce_max(float v, float *sh) {
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    v = wave_max(v);
+    if (lane == 0) sh[wave] = v;
+    __syncthreads();
+    float r = sh[0];
+    for (int w = 1; w < kEcThreads / kWave; ++w) r = fmaxf(r, sh[w]);
+    __syncthreads();
+    return r;
+}
+__device__ inline float block_reduce_sum(float v, float *sh) {
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    v = wave_sum(v);
+    if (lane == 0) sh[wave] = v;
+    __syncthreads();
+    float r = sh[0];
+    for (int w = 1; w < kEcThreads / kWave; ++w) r += sh[w];
+    __syncthreads();
+    return r;
+}
+// Exclusive prefix sum over the block's threads (in thread order).
+__device__ inline int block_exclusive_scan(int v, int *sh, int *total) {
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    int incl = v;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int n = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += n;
+    }
+    if (lane == kWave - 1) sh[wave] = incl;
+    __syncthreads();
+    int base = 0, tot = 0;
+    for (int w = 0; w < kEcThreads / kWave; ++w) {
+        if (w < wave) base += sh[w];
+        tot += sh[w];
+    }
+    __syncthreads();
+    *total = tot;
+    return base + incl - v;
+}
+
+__global__ __launch_bounds__(kEcThreads) void ec_select_kernel(const float *__restrict__ logits, int T, int E,
+                                                               int C, int32_t *__restrict__ ec_idx,
+                                                               float *__restrict__ ec_score) {
+    __shared__ float shf[kEcThreads / kWave];
+    __shared__ int shi[kEcThreads / kWave];
+    __shared__ uint32_t hist[256];
+    __shared__ uint32_t sel_prefix, sel_need;
+    __shared__ uint64_t cand[kEcMaxCapacity];
+    const int e = blockIdx.x;
+    const int tid = threadIdx.x;
+    const float *col = logits + e;
+
+    float m = -INFINITY;
+    for (int t = tid; t < T; t += kEcThreads) m = fmaxf(m, col[(int64_t)t * E]);
+    m = block_reduce_max(m, shf);
+    float z = 0.f;
+    for (int t = tid; t < T; t += kEcThreads) z += expf(col[(int64_t)t * E] - m);
+    z = block_reduce_sum(z, shf);
+
+    uint32_t prefix = 0, mask = 0, need = (uint32_t)C;
+    for (int pass = 0; pass < 4; ++pass) {
+        const int shift = 24 - 8 * pass;
+        for (int i = tid; i < 256; i += kEcThreads) hist[i] = 0;
+        __syncthreads();
+        for (int t = tid; t < T; t += kEcThreads) {
+            const uint32_t u = order_key(col[(int64_t)t * E]);
+            if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+        }
+        __syncthreads();
+        if (tid == 0) {
+            uint32_t cum = 0;
+            int b = 255;
+            for (; b > 0; --b) {
+                if (cum + hist[b] >= need) break;
+                cum += hist[b];
+            }
+            sel_need = need - cum;
+            sel_prefix = prefix | ((uint32_t)b << shift);
+        }
+        __syncthreads();
+        need = sel_need;
+        prefix = sel_prefix;
+        mask |= 255u << shift;
+        __syncthreads();
+    }
+    const uint32_t thr = prefix;       // order key of the C-th best token
+    const int n_gt = C - (int)need;    // tokens strictly above it; `need` ties are taken
+
+    const int chunk = (T + kEcThreads - 1) / kEcThreads;
+    const int t0 = tid * chunk;
+    const int t1 = min(T, t0 + chunk);
+    int gt = 0, eq = 0;
+    for (int t = t0; t < t1; ++t) {
+        const uint32_t u = order_key(col[(int64_t)t * E]);
+        gt += u > thr;
+        eq += u == thr;
+    }
+    int tot;
+    int gt_base = block_exclusive_scan(gt, shi, &tot);
+    int eq_base = block_exclusive_scan(eq, shi, &tot);
+    for (int t = t0; t < t1; ++t) {
+        const float v = col[(int64_t)t * E];
+        const uint32_t u = order_key(v);
+        if (u > thr) {
+            if (gt_base < n_gt) cand[gt_base] = rank_key(v, (uint32_t)t);
+            ++gt_base;
+        } else if (u == thr) {
+            if (eq_base < (int)need) cand[n_gt + eq_base] = rank_key(v, (uint32_t)t);
+            ++eq_base;
+        }
+    }
+    int P = 1;
+    while (P < C) P <<= 1;
+    for (int i = C + tid; i < P; i += kEcThreads) cand[i] = 0ull;
+    __syncthreads();
+    for (int size = 2; size <= P; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int i = tid; i < P / 2; i += kEcThreads) {
+                const int lo = 2 * stride * (i / stride) + (i % stride);
+                const int hi = lo + stride;
+                const bool desc = (lo & size) == 0;
+                const uint64_t a = cand[lo], b = cand[hi];
+                if ((a < b) == desc) {
+                    cand[lo] = b;
+                    cand[hi] = a;
+                }
+            }
+            __syncthreads();
+        }
+    }
+    for (int j = tid; j < C; j += kEcThreads) {
+        const uint64_t kk = cand[j];
+        const float v = key_value((uint32_t)(kk >> 32));
+        ec_idx[(int64_t)e * C + j] = (int32_t)rank_key_index(kk);
+        ec_score[(int64_t)e * C + j] = expf(v - m) / z;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// host launchers
+// ---------------------------------------------------------------------------
+template <int WM, int NT>
+static void launch_route_bf16_t(const RouteArgs &a, hipStream_t s) {
+    const int tok = 16 * WM;
+    const int grid = (a.T + tok - 1) / tok;
+    hipLaunchKernelGGL((route_bf16_kernel<WM, NT>), dim3(grid), dim3(256), 0, s, (const bf16 *)a.x,
+                       (const bf16 *)a.wg, a.bias, a.T, a.d, a.E, a.k, a.gating, a.logits, a.idx, a.w);
+}
+
+void launch_route(const RouteArgs &a, hipStream_t s) {
+    if (a.T == 0) return;
+    if (!a.bf16) {
+        hipLaunchKernelGGL(route_f32_kernel, dim3((a.T + 3) / 4), dim3(256), 0, s, (const float *)a.x,
+                           (const float *)a.wg, a.bias, a.T, a.d, a.E, a.k, a.gating, a.logits, a.idx, a.w);
+        return;
+    }
+    if (a.E <= 16) launch_route_bf16_t<1, 1>(a, s);
+    else if (a.E <= 32) launch_route_bf16_t<1, 2>(a, s);
+    else if (a.E <= 64) launch_route_bf16_t<1, 4>(a, s);
+    else if (a.E <= 128) launch_route_bf16_t<4, 8>(a, s);
+    else launch_route_bf16_t<4, 16>(a, s);
+}
+
+void launch_gate_logits(const float *logits, int T, int E, int k, int gating, int32_t *idx, float *w,
+                        hipStream_t s) {
+    if (T == 0) return;
+    hipLaunchKernelGGL(gate_logits_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, gating, idx, w);
+}
+
+void launch_ec_select(const float *logits, int T, int E, int C, int32_t *ec_idx, float *ec_score,
+                      hipStream_t s) {
+    hipLaunchKernelGGL(ec_select_kernel, dim3(E), dim3(kEcThreads), 0, s, logits, T, E, C, ec_idx, ec_score);
+}
+
+}  // namespace moe
