@@ -1,0 +1,210 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE layer forward pass on one MI355X.
+
+One step = one moe_forward call (router GEMM + gating, permutation and
+gather, grouped expert GEMMs, combine) over one batch of seeded synthetic
+tokens already resident in HBM.  Prints ONE JSON line on stdout.
+
+  python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME]
+                  [--no-cpu-baseline] [--cpu-seconds 15]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer tokens/sec + TFLOP/s (% bf16 MFMA peak), Mixtral-shape prefill"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def active_flops(spec, counts):
+    """Router GEMM plus the expert GEMMs of the kept assignments (and the shared
+    expert); elementwise work, softmax and the combine are not counted."""
+    mult = 3 if spec.act == "swiglu" else 2
+    router = 2.0 * spec.T * spec.d * spec.E
+    experts = 2.0 * float(sum(counts)) * spec.d * spec.F * mult
+    shared = 2.0 * spec.T * spec.d * spec.F_shared * 3 if spec.F_shared else 0.0
+    return router + experts + shared
+
+
+def gemm1_flops(spec, rows):
+    per_row = 2.0 * spec.d * spec.F * (2 if spec.act == "swiglu" else 1)
+    return rows * per_row
+
+
+def gemm1_bytes(spec, counts):
+    """Algorithmic bytes of the first grouped GEMM: the routed rows once, the
+    weights of every expert that received rows once, the hidden rows once."""
+    eb = 2 if spec.dtype == "bf16" else 4
+    nw = 2 if spec.act == "swiglu" else 1
+    rows = float(sum(counts))
+    touched = sum(1 for c in counts if c > 0)
+    return eb * (rows * spec.d + touched * nw * spec.F * spec.d + rows * spec.F)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral_8x7b_prefill_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run one device copy of this many MiB (HBM counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer is not sharded "
+              "across GPUs in this build", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import sparse_mixture_experts_gating_amd as moe
+    import workloads
+
+    spec = workloads.BY_NAME[args.workload]
+    dev = "cuda:0"
+    moe.load()
+    log(f"[bench] generating {spec.name} inputs on {dev}")
+    inp = workloads.make_inputs(spec, device=dev)
+    cfg = moe.config_from_spec(spec)
+    w = moe.make_weights(inp)
+    routing = moe.alloc_routing(cfg, dev)
+    r = moe.make_routing(routing)
+    ws = moe.alloc_workspace(cfg, moe.STAGE_FORWARD, dev)
+    y = torch.empty((spec.T, spec.d), dtype=spec.torch_dtype, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        moe.moe_forward(cfg, inp["x"], w, y, r, ws)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = elapsed * 1e3 / max(args.steps, 1)
+    counts = routing["counts"].cpu().numpy().tolist()
+    flops = active_flops(spec, counts)
+    tokens_per_s = spec.T / (ms / 1e3)
+    layer_tflops = flops / (ms / 1e3) / 1e12
+
+    # per-kernel durations from HIP events recorded on the launch stream
+    log("[bench] per-kernel event timing")
+    moe.moe_timing_reset()
+    moe.moe_timing_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    names = moe.moe_kernel_names()
+    kern = {}
+    for i, n in enumerate(names):
+        tot, cnt = moe.moe_timing_read(i)
+        if cnt:
+            kern[n] = dict(avg_us=round(tot * 1e3 / cnt, 3), launches_per_step=cnt / args.steps)
+    moe.moe_timing_enable(False)
+    dominant = max(kern, key=lambda n: kern[n]["avg_us"] * kern[n]["launches_per_step"])
+    avg_s = kern[dominant]["avg_us"] * 1e-6
+    if dominant == "gemm1_act":
+        ach = gemm1_flops(spec, sum(counts)) / avg_s / 1e12
+        bound = "mfma"
+        peak = PEAK_BF16_TFLOPS if spec.dtype == "bf16" else PEAK_F32_TFLOPS
+        unit = "TFLOP/s"
+    elif dominant == "gemm2":
+        ach = gemm1_flops(spec, sum(counts)) / (2 if spec.act == "swiglu" else 1) / avg_s / 1e12
+        bound = "mfma"
+        peak = PEAK_BF16_TFLOPS if spec.dtype == "bf16" else PEAK_F32_TFLOPS
+        unit = "TFLOP/s"
+    else:
+        ach, bound, peak, unit = None, "hbm", PEAK_HBM_GBS, "GB/s"
+    roofline = dict(bound=bound, kernel=dominant, achieved=None if ach is None else round(ach, 2), peak=peak,
+                    unit=unit, frac=None if ach is None else round(ach / peak, 4), traffic=None,
+                    avg_launch_us=kern[dominant]["avg_us"])
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(spec, inp, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.dtype,
+        "data": "synthetic (seeded Gaussian tokens, N(0,1/fan_in) weights)",
+        "config": {"workload": spec.name, "tokens": spec.T, "d_model": spec.d, "experts": spec.E,
+                   "top_k": spec.k, "d_ff": spec.F, "d_ff_shared": spec.F_shared, "gating": spec.gating,
+                   "activation": spec.act, "parallelism": "none (1 GPU)"},
+        "layer_tflops_active": round(layer_tflops, 2),
+        "layer_frac_bf16_peak": round(layer_tflops / PEAK_BF16_TFLOPS, 4),
+        "kernels_us": {n: v["avg_us"] for n, v in kern.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(spec, inp, seconds):
+    """The oracle as it stands on the host cores, on a bounded sample of tokens
+    of the same workload (host copies of the same inputs)."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    log("[bench] cpu baseline: copying inputs to the host")
+    host = {k: (None if v is None else v.detach().cpu().float().numpy()) for k, v in inp.items()}
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    os.environ.setdefault("OMP_NUM_THREADS", str(threads))
+    oracle._load()
+    rng = np.random.default_rng(0)
+    n = 8
+    while True:
+        toks = np.sort(rng.choice(spec.T, size=n, replace=False))
+        t0 = time.perf_counter()
+        oracle.forward_tokens(spec, host, toks)
+        dt = time.perf_counter() - t0
+        log(f"[bench] cpu baseline: {n} tokens took {dt:.2f} s")
+        if dt >= 0.6 * seconds or n == spec.T:
+            break
+        n = int(min(spec.T, max(2 * n, n * seconds / max(dt, 1e-3))))
+    return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} of {spec.T} tokens of {spec.name}, all layer steps, float64 C loops "
+                      f"(OpenMP over the rows of each expert), {dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()
