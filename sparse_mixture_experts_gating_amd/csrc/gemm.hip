@@ -10,23 +10,24 @@
 // youngju.dev "Sparse Mixture of Experts（MoE）アーキテクチャ深層分析" SwiGLUExpert).
 //
 // Tiles: a device-side plan (mstart) lists the m-tiles of every expert; the
-// grid covers the worst case and surplus blocks exit.  Tile order is (expert,
-// n-tile, m-tile) with m fastest, remapped so that runs of consecutive tiles
-// land on one XCD and share its L2 copy of the weight panel.
+// grid covers the worst case and surplus blocks exit.  Inside an expert with
+// Me m-tiles, tiles run in groups of Me x gN (m fastest, gN ~ 32 / Me weight
+// panels), and every XCD receives runs of 32 consecutive tiles: a run shares
+// the expert's activation tiles and a few weight panels in that XCD's L2.
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 
 constexpr int kXcds = 8;
-constexpr int kXcdRun = 4;  // consecutive logical tiles per XCD
+constexpr int kXcdRun = 32;  // consecutive logical tiles per XCD
 constexpr int kGridQuantum = kXcds * kXcdRun;
 
-// Blocks are dispatched round-robin over the XCDs (block b -> XCD b % 8).
-// Within each group of 32 blocks, XCD x receives logical tiles 4x .. 4x+3.
+// Blocks are dispatched round-robin over the XCDs (block b -> XCD b % 8):
+// the i-th block an XCD receives gets logical tile 256*(i/32) + 32*xcd + i%32.
 __device__ inline int xcd_remap(int b) {
-    const int grp = b / kGridQuantum, within = b % kGridQuantum;
-    return grp * kGridQuantum + (within % kXcds) * kXcdRun + within / kXcds;
+    const int xcd = b % kXcds, slot = b / kXcds;
+    return (slot / kXcdRun) * kGridQuantum + xcd * kXcdRun + slot % kXcdRun;
 }
 
 struct TileCoord {
@@ -35,17 +36,29 @@ struct TileCoord {
     bool valid;
 };
 
+// Position of tile `local` among the mt x ntn tiles of one group.
+__device__ inline void group_tile(int local, int mt, int ntn, int *m, int *n) {
+    int gn = kXcdRun / mt;
+    if (gn < 1) gn = 1;
+    const int per = mt * gn;
+    const int grp = local / per, within = local % per;
+    *m = within % mt;
+    *n = grp * gn + within / mt;
+}
+
 template <int BM>
 __device__ inline TileCoord find_tile(int tile, const int32_t *offsets, const int32_t *mstart, int G,
                                       int64_t rows, int ntn) {
     TileCoord c;
     c.valid = false;
+    int m, n;
     if (offsets == nullptr) {
         const int mtiles = (int)((rows + BM - 1) / BM);
         if (tile >= mtiles * ntn) return c;
+        group_tile(tile, mtiles, ntn, &m, &n);
         c.g = 0;
-        c.nt = tile / mtiles;
-        c.row0 = (int64_t)(tile % mtiles) * BM;
+        c.nt = n;
+        c.row0 = (int64_t)m * BM;
         c.row_end = rows;
         c.valid = true;
         return c;
@@ -60,9 +73,10 @@ __device__ inline TileCoord find_tile(int tile, const int32_t *offsets, const in
     }
     const int local = tile - mstart[lo] * ntn;
     const int mt_g = mstart[lo + 1] - mstart[lo];
+    group_tile(local, mt_g, ntn, &m, &n);
     c.g = lo;
-    c.nt = local / mt_g;
-    c.row0 = offsets[lo] + (int64_t)(local % mt_g) * BM;
+    c.nt = n;
+    c.row0 = offsets[lo] + (int64_t)m * BM;
     c.row_end = offsets[lo + 1];
     c.valid = true;
     return c;
@@ -87,15 +101,23 @@ struct GemmParams {
     int act;
 };
 
-template <int BM, int BN, int WM, int WN, bool GLU>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmParams p) {
+// PD: K tiles in flight in registers (1: one set, loads issued a step ahead;
+// 2: two sets, loads issued two steps ahead).  SB: pin the loads at the head
+// of each step (scheduling barrier).  FB: double-buffer MFMA fragments.
+template <int BM, int BN, int WM, int WN, bool GLU, bool FB, int PD = 2, bool SB = true>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
+    constexpr int NT = 64 * WM * WN;  // threads
     constexpr int BK = 64;
     constexpr int NB = GLU ? 2 * BN : BN;
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int TM = WTM / 32, TN = WTN / 32;
-    constexpr int A_PER_T = BM * 8 / 256, B_PER_T = NB * 8 / 256;
-    static_assert(WM * WN == 4, "four waves");
-    static_assert(A_PER_T >= 1 && B_PER_T >= 1, "tile too small");
+    constexpr int TB = GLU ? 2 * TN : TN;  // B fragments per k-substep (gate then up)
+    constexpr int RSTEP = NT / 8;          // rows between a thread's successive 16-byte chunks
+    constexpr int A_PER_T = BM / RSTEP, B_PER_T = NB / RSTEP;
+    constexpr int FS = FB ? 2 : 1;         // fragment register sets
+    static_assert(A_PER_T >= 1 && B_PER_T >= 1 && BM % RSTEP == 0 && NB % RSTEP == 0, "tile/threads");
+    static_assert(!GLU || BN % RSTEP == 0, "gate/up split must fall between a thread's chunks");
+    static_assert(TM >= 1 && TN >= 1, "wave tile");
     __shared__ __attribute__((aligned(16))) bf16 lds[2][(BM + NB) * BK];
 
     const int ntn = (p.N + BN - 1) / BN;
@@ -103,96 +125,148 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmParams p) {
     if (!tc.valid) return;
     const int n0 = tc.nt * BN;
     const int64_t K = p.K;
-    const bf16 *B0g = p.B0 + (int64_t)tc.g * p.N * K;
-    const bf16 *B1g = GLU ? p.B1 + (int64_t)tc.g * p.N * K : nullptr;
 
     const int tid = threadIdx.x;
     const int wave = tid / kWave, lane = tid % kWave;
     const int wm = wave % WM, wn = wave / WM;
 
-    // global source of each thread's chunks (row clamped into the group)
-    const bf16 *asrc[A_PER_T];
-    int adst[A_PER_T];
+    // Loads: uniform tile bases plus 32-bit per-chunk byte offsets (rows
+    // clamped into the group / matrix).  Thread tid moves chunk (tid % 8) of
+    // rows tid/8 + RSTEP*i.
+    const int r0 = tid / 8, ch0 = tid % 8;
+    const char *abase = (const char *)(p.A + tc.row0 * K);
+    const char *b0base = (const char *)(p.B0 + ((int64_t)tc.g * p.N + n0) * K);
+    const char *b1base = GLU ? (const char *)(p.B1 + ((int64_t)tc.g * p.N + n0) * K) : nullptr;
+    uint32_t aoff[A_PER_T], boff[B_PER_T];
 #pragma unroll
     for (int i = 0; i < A_PER_T; ++i) {
-        const int q = tid + i * 256, r = q / 8, ch = q % 8;
-        int64_t gr = tc.row0 + r;
-        if (gr >= tc.row_end) gr = tc.row_end - 1;
-        asrc[i] = p.A + gr * K + ch * 8;
-        adst[i] = r * BK + ((ch ^ swz(r)) * 8);
+        int64_t r = r0 + RSTEP * i;
+        if (tc.row0 + r >= tc.row_end) r = tc.row_end - 1 - tc.row0;
+        aoff[i] = (uint32_t)((r * K + ch0 * 8) * 2);
     }
-    const bf16 *bsrc[B_PER_T];
-    int bdst[B_PER_T];
 #pragma unroll
     for (int i = 0; i < B_PER_T; ++i) {
-        const int q = tid + i * 256, r = q / 8, ch = q % 8;
-        const bool up = GLU && r >= BN;
-        int n = n0 + (up ? r - BN : r);
-        if (n >= p.N) n = p.N - 1;
-        bsrc[i] = (up ? B1g : B0g) + (int64_t)n * K + ch * 8;
-        bdst[i] = (BM + r) * BK + ((ch ^ swz(r)) * 8);
+        int r = r0 + RSTEP * i;
+        if (GLU && r >= BN) r -= BN;
+        if (n0 + r >= p.N) r = p.N - 1 - n0;
+        boff[i] = (uint32_t)(((int64_t)r * K + ch0 * 8) * 2);
     }
+    // LDS: chunk c of row r sits at chunk slot c ^ swz(r); swz is the same for
+    // all of a thread's rows (they differ by multiples of 16), so one base
+    // address plus compile-time strides covers them.
+    const int sdst = r0 * BK + ((ch0 ^ swz(r0)) * 8);
+    const int sw_a = swz(wm * WTM + lane % 32);
+    const int sw_b = swz(wn * WTN + lane % 32);
+    const int fa0 = (wm * WTM + lane % 32) * BK, fb0 = (BM + wn * WTN + lane % 32) * BK;
 
-    f32x16 acc[TM][TN];
-    f32x16 accu[GLU ? TM : 1][GLU ? TN : 1];
+    f32x16 acc[TM][TB];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            acc[i][j] = f32x16{};
-            if constexpr (GLU) accu[i][j] = f32x16{};
-        }
+        for (int j = 0; j < TB; ++j) acc[i][j] = f32x16{};
 
-    u32x4 ra[A_PER_T], rb[B_PER_T];
-    auto gload = [&](int kt) {
-        const int64_t ko = (int64_t)kt * BK;
+    // Two register sets keep two K tiles in flight (prefetch distance 2); the
+    // loads are issued unconditionally (the tail re-reads the last tile) so the
+    // compiler's wait counts stay exact.  Two LDS buffers alternate: while the
+    // MFMAs consume one, the next tile is stored into the other.
+    u32x4 ra[2][A_PER_T], rb[2][B_PER_T];
+    auto gload = [&](int kt, int set) {
+        const int64_t ko = (int64_t)kt * BK * 2;
+        const char *ab = abase + ko, *b0 = b0base + ko, *b1 = GLU ? b1base + ko : nullptr;
 #pragma unroll
-        for (int i = 0; i < A_PER_T; ++i) ra[i] = load16(asrc[i] + ko);
+        for (int i = 0; i < A_PER_T; ++i) ra[set][i] = load16(ab + aoff[i]);
 #pragma unroll
-        for (int i = 0; i < B_PER_T; ++i) rb[i] = load16(bsrc[i] + ko);
+        for (int i = 0; i < B_PER_T; ++i) {
+            const bool up = GLU && RSTEP * i >= BN;
+            rb[set][i] = load16((up ? b1 : b0) + boff[i]);
+        }
     };
-    auto lstore = [&](int buf) {
+    auto lstore = [&](int buf, int set) {
+        bf16 *L = lds[buf];
 #pragma unroll
-        for (int i = 0; i < A_PER_T; ++i) store16(&lds[buf][adst[i]], ra[i]);
+        for (int i = 0; i < A_PER_T; ++i) store16(L + sdst + i * RSTEP * BK, ra[set][i]);
 #pragma unroll
-        for (int i = 0; i < B_PER_T; ++i) store16(&lds[buf][bdst[i]], rb[i]);
+        for (int i = 0; i < B_PER_T; ++i) store16(L + BM * BK + sdst + i * RSTEP * BK, rb[set][i]);
+    };
+    bf16x8 fa[FS][TM], fb[FS][TB];
+    auto fload = [&](const bf16 *L, int ks, int slot) {
+        const int ch = ks * 2 + lane / 32;
+        const bf16 *La = L + fa0 + ((ch ^ sw_a) * 8);
+        const bf16 *Lb = L + fb0 + ((ch ^ sw_b) * 8);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) fa[slot][i] = __builtin_bit_cast(bf16x8, load16(La + i * 32 * BK));
+#pragma unroll
+        for (int j = 0; j < TB; ++j)
+            fb[slot][j] = __builtin_bit_cast(bf16x8,
+                                             load16(Lb + ((j >= TN ? BN : 0) + (j % TN) * 32) * BK));
+    };
+    auto mfmas = [&](int slot) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TB; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0);
+    };
+    // MFMAs of one K tile whose k-substep-0 fragments are already in slot 0
+    auto compute = [&](const bf16 *L) {
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            if constexpr (FB) {
+                if (ks + 1 < BK / 16) fload(L, ks + 1, (ks + 1) & 1);
+                mfmas(ks & 1);
+            } else {
+                if (ks > 0) fload(L, ks, 0);
+                mfmas(0);
+            }
+        }
     };
 
     const int KT = p.K / BK;
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < KT) gload(kt + 1);
-        const bf16 *L = lds[cur];
-#pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-            const int ch = ks * 2 + lane / 32;
-            bf16x8 af[TM], bfr[TN], bu[GLU ? TN : 1];
-#pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                const int r = wm * WTM + i * 32 + lane % 32;
-                af[i] = __builtin_bit_cast(bf16x8, load16(L + r * BK + ((ch ^ swz(r)) * 8)));
-            }
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const int r = wn * WTN + j * 32 + lane % 32;
-                bfr[j] = __builtin_bit_cast(bf16x8, load16(L + (BM + r) * BK + ((ch ^ swz(r)) * 8)));
-                if constexpr (GLU)
-                    bu[j] = __builtin_bit_cast(bf16x8, load16(L + (BM + BN + r) * BK + ((ch ^ swz(r)) * 8)));
-            }
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-                    if constexpr (GLU)
-                        accu[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bu[j], accu[i][j], 0, 0, 0);
-                }
-        }
-        if (kt + 1 < KT) lstore(cur ^ 1);
+    if constexpr (PD == 1) {
+        // one register set: tile kt+1 is loaded during step kt and stored into
+        // the other LDS buffer at its end (the tail re-reads tile KT-1)
+        gload(0, 0);
+        lstore(0, 0);
         __syncthreads();
+        for (int kt = 0; kt < KT; ++kt) {
+            const int cur = kt & 1;
+            gload(min(kt + 1, KT - 1), 0);
+            if constexpr (SB) __builtin_amdgcn_sched_barrier(0);
+            fload(lds[cur], 0, 0);
+            compute(lds[cur]);
+            lstore(cur ^ 1, 0);
+            __syncthreads();
+        }
+    } else {
+        gload(0, 0);
+        gload(KT > 1 ? 1 : 0, 1);
+        lstore(0, 0);
+        __syncthreads();
+        // Pairs of K tiles with no control flow inside, so the compiler's wait
+        // counts see exactly one register set in flight when the other is
+        // stored.  Loads and stores past the last tile re-read and re-store
+        // tile KT-1 into a buffer nobody reads afterwards.
+        int kt = 0;
+        for (; kt + 1 < KT; kt += 2) {
+            // even step: LDS buffer 0 holds tile kt, register set 1 holds tile kt+1
+            gload(min(kt + 2, KT - 1), 0);
+            if constexpr (SB) __builtin_amdgcn_sched_barrier(0);
+            fload(lds[0], 0, 0);
+            lstore(1, 1);
+            compute(lds[0]);
+            __syncthreads();
+            // odd step: LDS buffer 1 holds tile kt+1, register set 0 holds tile kt+2 (or KT-1)
+            gload(min(kt + 3, KT - 1), 1);
+            if constexpr (SB) __builtin_amdgcn_sched_barrier(0);
+            fload(lds[1], 0, 0);
+            lstore(0, 0);
+            compute(lds[1]);
+            __syncthreads();
+        }
+        if (kt < KT) {  // odd tile count: the last tile is in LDS buffer 0
+            fload(lds[0], 0, 0);
+            compute(lds[0]);
+        }
     }
 
     // epilogue: D[8*q + 4*(lane/32) + j][lane%32] of each 32x32 tile is acc[4*q + j]
@@ -211,7 +285,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmParams p) {
                     const int64_t row = tc.row0 + wm * WTM + i * 32 + 8 * q + 4 * (lane / 32) + jj;
                     if (row >= tc.row_end) continue;
                     float v = acc[i][j][4 * q + jj];
-                    if constexpr (GLU) v = silu(v) * accu[i][j][4 * q + jj];
+                    if constexpr (GLU) v = silu(v) * acc[i][TN + j][4 * q + jj];
                     else v = apply_act(p.act, v + bcol);
                     p.C[row * p.N + col] = (bf16)v;
                 }
@@ -349,13 +423,14 @@ static int64_t grid_for(const GemmArgs &a, int BM, int BN) {
     return g;
 }
 
-template <int BM, int BN, int WM, int WN, bool GLU>
+template <int BM, int BN, int WM, int WN, bool GLU, bool FB = true, int PD = 2, bool SB = false>
 static void launch_bf16_t(const GemmArgs &a, hipStream_t s) {
     GemmParams p{(const bf16 *)a.A, (const bf16 *)a.B0, (const bf16 *)a.B1, a.bias, (bf16 *)a.C,
                  a.offsets, a.mstart, a.G, a.rows, a.N, a.K, a.act};
     const int64_t grid = grid_for(a, BM, BN);
     if (grid == 0) return;
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, GLU>), dim3((unsigned)grid), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, GLU, FB, PD, SB>), dim3((unsigned)grid), dim3(64 * WM * WN), 0, s,
+                       p);
 }
 
 template <bool GLU>
@@ -374,15 +449,18 @@ void launch_grouped_gemm(const GemmArgs &a, int shape, hipStream_t s) {
         else launch_f32_t<false>(a, s);
         return;
     }
+    // Tile shapes measured on the Mixtral-shape prefill GEMMs (T=4096, k=2,
+    // d=4096, F=14336): 8 waves (2 per SIMD) with 256-row tiles, two K tiles
+    // in flight, fragments double-buffered, loads left to the scheduler.
     if (shape == kGemmDecode) {
         if (glu) launch_bf16_t<32, 128, 1, 4, true>(a, s);
         else launch_bf16_t<32, 128, 1, 4, false>(a, s);
     } else if (shape == kGemmSmallM) {
-        if (glu) launch_bf16_t<128, 128, 2, 2, true>(a, s);
-        else launch_bf16_t<128, 256, 2, 2, false>(a, s);
+        if (glu) launch_bf16_t<128, 128, 2, 2, true, true, 2, true>(a, s);
+        else launch_bf16_t<128, 256, 2, 2, false, true, 2, true>(a, s);
     } else {
-        if (glu) launch_bf16_t<256, 128, 2, 2, true>(a, s);
-        else launch_bf16_t<256, 256, 2, 2, false>(a, s);
+        if (glu) launch_bf16_t<256, 128, 2, 4, true, true, 2, false>(a, s);
+        else launch_bf16_t<256, 256, 2, 4, false, true, 2, false>(a, s);
     }
 }
 
