@@ -80,6 +80,12 @@ def _load():
     lib.oracle_combine_topk.restype = None
     lib.oracle_combine_expert_choice.argtypes = [i64, i32, i32, i32, p, p, p, p, p]
     lib.oracle_combine_expert_choice.restype = None
+    lib.oracle_capacity_topk.argtypes = [f64, i64, i32, i32, i32]
+    lib.oracle_capacity_topk.restype = i32
+    lib.oracle_router_losses.argtypes = [i64, i32, i32, p, p, p, p, p]
+    lib.oracle_router_losses.restype = ctypes.c_int
+    lib.oracle_logits_noisy.argtypes = [i64, i32, i32, p, p, p, p, p, p]
+    lib.oracle_logits_noisy.restype = None
     _lib = lib
     return lib
 
@@ -136,6 +142,37 @@ def route_topk(lg, k: int, gating: str = "topk_softmax"):
 def capacity(capacity_factor: float, tokens: int, num_experts: int) -> int:
     """int(cf * tokens / E), truncated toward zero ([yj-zh] SwitchRouter)."""
     return int(_load().oracle_capacity(float(capacity_factor), int(tokens), int(num_experts)))
+
+
+def capacity_topk(capacity_factor: float, tokens: int, k: int, num_experts: int, min_capacity: int = 0) -> int:
+    """max(min_capacity, int(cf * tokens * k / E)) ([devtips] capacity example; k = 1 is Switch)."""
+    return int(_load().oracle_capacity_topk(float(capacity_factor), int(tokens), int(k), int(num_experts),
+                                            int(min_capacity)))
+
+
+def router_losses(lg, idx):
+    """(aux, z_loss, mean_probs): E * sum f_e P_e and mean logsumexp^2 ([yj-ja]
+    compute_load_balancing_loss, router_z_loss)."""
+    lg, idx = _f32(lg), _i32(idx)
+    T, E = lg.shape
+    k = idx.shape[1]
+    aux, z = ctypes.c_double(), ctypes.c_double()
+    P = np.empty(E, np.float64)
+    rc = _load().oracle_router_losses(T, E, k, _ptr(lg), _ptr(idx), ctypes.addressof(aux), ctypes.addressof(z),
+                                      _ptr(P))
+    if rc != 0:
+        raise ValueError("oracle_router_losses: bad arguments")
+    return aux.value, z.value, P
+
+
+def logits_noisy(x, wg, bias, wn, noise) -> np.ndarray:
+    """Noisy router logits x Wg^T + b + softplus(x Wn^T) * noise ([yj-ja] TopKGating)."""
+    x, wg, bias, wn, noise = _f32(x), _f32(wg), _f32(bias), _f32(wn), _f32(noise)
+    T, d = x.shape
+    E = wg.shape[0]
+    out = np.empty((T, E), np.float32)
+    _load().oracle_logits_noisy(T, d, E, _ptr(x), _ptr(wg), _ptr(bias), _ptr(wn), _ptr(noise), _ptr(out))
+    return out
 
 
 def permute(idx, num_experts: int, cap: int = 0, group: int = 0):
@@ -218,12 +255,19 @@ def combine_expert_choice(ec_idx, ec_score, Y, T: int, Ys=None) -> np.ndarray:
 # ----------------------------------------------------------------------------
 
 def _spec_capacity(spec) -> int:
-    if spec.gating == "switch":
+    min_cap = getattr(spec, "min_capacity", 0)
+    if spec.gating == "switch" or (spec.gating in ("topk_softmax", "softmax_topk") and spec.capacity_factor > 0):
         group = spec.capacity_group if spec.capacity_group > 0 else spec.T
-        return capacity(spec.capacity_factor, group, spec.E)
+        return capacity_topk(spec.capacity_factor, group, spec.k, spec.E, min_cap)
     if spec.gating == "expert_choice":
         return capacity(spec.capacity_factor, spec.T, spec.E)
     return 0
+
+
+def _router_logits(spec, inp, x):
+    if getattr(spec, "noisy", False):
+        return logits_noisy(x, inp["wg"], inp.get("bg"), inp["wn"], inp["noise"])
+    return logits(x, inp["wg"], inp.get("bg"))
 
 
 def _experts_rows(spec, inp, X, expert_of_row):
@@ -256,7 +300,7 @@ def forward(spec, inp, lg=None) -> dict:
     """
     x = _f32(inp["x"])
     if lg is None:
-        lg = logits(x, inp["wg"], inp.get("bg"))
+        lg = _router_logits(spec, inp, x)
     lg = _f32(lg)
     out = dict(logits=lg)
     cap = _spec_capacity(spec)
@@ -275,7 +319,7 @@ def forward(spec, inp, lg=None) -> dict:
                    row_token=rows_tok.copy(), y_rows=Y, y_shared=Ys, y=y.astype(np.float32), y64=y)
         return out
     idx, w = route_topk(lg, spec.k, spec.gating)
-    group = spec.capacity_group if spec.gating == "switch" else 0
+    group = spec.capacity_group if cap > 0 else 0
     perm = permute(idx, spec.E, cap, group)
     inpf = {kk: (_f32(v) if v is not None else None) for kk, v in inp.items()}
     rt = perm["row_token"]
@@ -301,9 +345,9 @@ def forward_tokens(spec, inp, tokens, lg=None) -> dict:
     tokens = np.asarray(tokens, dtype=np.int64)
     x = inp["x"]
     xs = _f32(x[_index_like(x, tokens)])
-    need_all = spec.gating in ("switch", "expert_choice")
-    if lg is None and need_all:
-        lg = logits(x, inp["wg"], inp.get("bg"))
+    need_all = spec.gating in ("switch", "expert_choice") or spec.capacity_factor > 0
+    if lg is None and (need_all or getattr(spec, "noisy", False)):
+        lg = _router_logits(spec, inp, _f32(x))
     if lg is not None:
         lg = _f32(lg)
         lg_sel = lg[tokens]
@@ -324,7 +368,7 @@ def forward_tokens(spec, inp, tokens, lg=None) -> dict:
                 if i is not None:
                     terms.append((i, float(ec_score[e, j]), e))
     else:
-        if spec.gating == "switch":
+        if cap > 0:
             idx_all, w_all = route_topk(lg, spec.k, spec.gating)
             perm = permute(idx_all, spec.E, cap, spec.capacity_group)
             idx, w, kept = idx_all[tokens], w_all[tokens], perm["slot_row"][tokens] >= 0

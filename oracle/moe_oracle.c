@@ -336,3 +336,82 @@ void oracle_combine_expert_choice(int64_t T, int32_t E, int32_t C, int32_t d,
         }
     }
 }
+
+/* Capacity of token-choice gating with k experts per token:
+ * int(capacity_factor * tokens * k / E), at least min_capacity.  The
+ * [devtips] capacity example scales by top_k (and prints a float; the
+ * integer part is taken here, as [yj-zh] SwitchRouter does); k = 1 is the
+ * Switch capacity.  A minimum capacity appears in the [yj-zh] DeepSpeed MoE
+ * configuration example (min_capacity). */
+int32_t oracle_capacity_topk(double capacity_factor, int64_t tokens, int32_t k, int32_t E, int32_t min_capacity) {
+    int32_t c = (int32_t)(capacity_factor * (double)tokens * (double)k / (double)E);
+    return c < min_capacity ? min_capacity : c;
+}
+
+/* Router side outputs ([yj-ja] compute_load_balancing_loss and router_z_loss;
+ * [yj-zh] load_balancing_loss):
+ *   P_e  = mean over tokens of softmax(l_t)_e;
+ *   f_e  = (number of (t, j) with idx[t][j] == e) / (T * k), counted on the
+ *          selection before any capacity drop;
+ *   aux  = E * sum_e f_e * P_e   (1 when routing and probabilities are uniform);
+ *   zl   = mean over tokens of logsumexp(l_t)^2.
+ * prob_mean may be NULL.  Returns 0, or -1 on bad arguments. */
+int oracle_router_losses(int64_t T, int32_t E, int32_t k, const float *logits, const int32_t *idx, double *aux,
+                         double *zloss, double *prob_mean) {
+    if (T < 1 || E < 1 || k < 1) return -1;
+    double *P = (double *)calloc((size_t)E, sizeof(double));
+    double *f = (double *)calloc((size_t)E, sizeof(double));
+    if (!P || !f) { free(P); free(f); return -1; }
+    double zsum = 0.0;
+    for (int64_t t = 0; t < T; ++t) {
+        const float *l = logits + t * E;
+        double m = (double)l[0];
+        for (int32_t e = 1; e < E; ++e)
+            if ((double)l[e] > m) m = (double)l[e];
+        double s = 0.0;
+        for (int32_t e = 0; e < E; ++e) s += exp((double)l[e] - m);
+        for (int32_t e = 0; e < E; ++e) P[e] += exp((double)l[e] - m) / s;
+        const double lse = m + log(s);
+        zsum += lse * lse;
+        for (int32_t j = 0; j < k; ++j) {
+            const int32_t e = idx[t * k + j];
+            if (e < 0 || e >= E) { free(P); free(f); return -1; }
+            f[e] += 1.0;
+        }
+    }
+    double a = 0.0;
+    for (int32_t e = 0; e < E; ++e) {
+        P[e] /= (double)T;
+        f[e] /= (double)(T * k);
+        a += f[e] * P[e];
+        if (prob_mean) prob_mean[e] = P[e];
+    }
+    *aux = (double)E * a;
+    *zloss = zsum / (double)T;
+    free(P);
+    free(f);
+    return 0;
+}
+
+/* Noisy router logits ([yj-ja] TopKGating, training branch; [garden]
+ * "7. 안정화 기법" Noisy Top-k; [yj-ja] gating formula "+ noise"):
+ *   l[t][e] = x_t . Wg_e + b_e + softplus(x_t . Wn_e) * n[t][e]
+ * with the standard-normal draw n supplied by the caller.  softplus(u) =
+ * log(1 + exp(u)), evaluated as max(u, 0) + log1p(exp(-|u|)).  Sums in double,
+ * rounded once to float32. */
+void oracle_logits_noisy(int64_t T, int32_t d, int32_t E, const float *x, const float *wg, const float *bias,
+                         const float *wn, const float *noise, float *logits) {
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t e = 0; e < E; ++e) {
+            double s = 0.0, u = 0.0;
+            for (int32_t i = 0; i < d; ++i) {
+                s += (double)x[t * d + i] * (double)wg[(int64_t)e * d + i];
+                u += (double)x[t * d + i] * (double)wn[(int64_t)e * d + i];
+            }
+            if (bias) s += (double)bias[e];
+            const double sp = (u > 0.0 ? u : 0.0) + log1p(exp(-fabs(u)));
+            logits[t * E + e] = (float)(s + sp * (double)noise[t * E + e]);
+        }
+    }
+}

@@ -14,8 +14,10 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "moe_oracle.c")
 
 MUTATIONS = [
-    ("bias_dropped", "if (bias) s += (double)bias[e];", ";"),
-    ("router_transposed", "(double)wg[(int64_t)e * d + i]", "(double)wg[(int64_t)i * E + e]"),
+    ("bias_dropped", "if (bias) s += (double)bias[e];\n            logits[t * E + e] = (float)s;",
+     "logits[t * E + e] = (float)s;"),
+    ("router_transposed", "(double)wg[(int64_t)e * d + i];\n            if (bias)",
+     "(double)wg[(int64_t)i * E + e];\n            if (bias)"),
     ("ties_to_higher_index", "return ia < ib;", "return ia > ib;"),
     ("softmax_sign", "z += exp((double)l[idx[t * k + j]] - top);", "z += exp(top - (double)l[idx[t * k + j]]);"),
     ("switch_renormalised", "for (int32_t e = 0; e < E; ++e) z += exp((double)l[e] - top);",
@@ -31,6 +33,16 @@ MUTATIONS = [
     ("combine_slot_weight", "double g = (double)w[t * k + j];", "double g = (double)w[t * k];"),
     ("shared_dropped", "if (Ys)\n            for (int32_t o = 0; o < d; ++o) y[t * d + o] += Ys[t * d + o];", ";"),
     ("ec_softmax_over_experts", "z += exp((double)logits[t * E + e] - m);", "z += exp((double)logits[t * E + e] - m) * (t < E);"),
+    ("aux_without_E", "*aux = (double)E * a;", "*aux = a;"),
+    ("zloss_not_squared", "zsum += lse * lse;", "zsum += lse;"),
+    ("f_not_normalised_by_k", "f[e] /= (double)(T * k);", "f[e] /= (double)T;"),
+    ("topk_capacity_without_k", "(double)tokens * (double)k / (double)E);\n    return c < min_capacity",
+     "(double)tokens / (double)E);\n    return c < min_capacity"),
+    ("min_capacity_ignored", "return c < min_capacity ? min_capacity : c;", "return c;"),
+    ("softplus_as_relu", "const double sp = (u > 0.0 ? u : 0.0) + log1p(exp(-fabs(u)));",
+     "const double sp = (u > 0.0 ? u : 0.0);"),
+    ("noise_projection_transposed", "u += (double)x[t * d + i] * (double)wn[(int64_t)e * d + i];",
+     "u += (double)x[t * d + i] * (double)wn[(int64_t)i * E + e];"),
     ("ec_ties_to_higher_token", "if (best < 0 || ranks_before(logits[t * E + e], t, logits[best * E + e], best))",
      "if (best < 0 || logits[t * E + e] >= logits[best * E + e])"),
 ]

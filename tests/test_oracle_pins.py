@@ -426,3 +426,94 @@ def test_integer_inputs_make_router_exact():
     ref = inp["x"].double().numpy() @ inp["wg"].double().numpy().T
     assert np.array_equal(lg.astype(np.float64), ref)
     assert np.all(ref * 8 == np.round(ref * 8))
+
+
+# ---------------------------------------------------------------------------
+# router side outputs, top-k capacity, noisy router
+# ---------------------------------------------------------------------------
+
+def test_router_losses_closed_forms():
+    """Uniform probabilities and a balanced selection give aux = 1 and, with zero
+    logits, z = (ln E)^2 ([yj-ja] compute_load_balancing_loss: minimal when balanced)."""
+    T, E, k = 64, 8, 2
+    lg = np.zeros((T, E), np.float32)
+    idx = (np.arange(T * k).reshape(T, k) % E).astype(np.int32)
+    aux, z, P = oracle.router_losses(lg, idx)
+    assert abs(aux - 1.0) < 1e-12
+    assert abs(z - math.log(E) ** 2) < 1e-12
+    assert np.allclose(P, 1.0 / E)
+    # everything on expert 3 with probability ~1: aux -> E
+    lg2 = np.zeros((T, E), np.float32)
+    lg2[:, 3] = 60.0
+    idx2 = np.full((T, 1), 3, np.int32)
+    aux2, _, _ = oracle.router_losses(lg2, idx2)
+    assert abs(aux2 - E) < 1e-9
+
+
+def test_router_losses_match_scipy():
+    T, E, k = 300, 16, 4
+    lg = workloads.random_logits(T, E, seed=31).numpy()
+    idx, _ = oracle.route_topk(lg, k, "topk_softmax")
+    aux, z, P = oracle.router_losses(lg, idx)
+    lg64 = lg.astype(np.float64)
+    Pref = scipy.special.softmax(lg64, axis=1).mean(0)
+    f = np.bincount(idx.ravel(), minlength=E) / (T * k)
+    assert np.allclose(P, Pref, rtol=1e-12)
+    assert abs(aux - E * float((f * Pref).sum())) < 1e-12
+    assert abs(z - float((scipy.special.logsumexp(lg64, axis=1) ** 2).mean())) < 1e-9
+
+
+def test_topk_capacity_formula():
+    # [devtips] capacity example: (batch * seq * top_k / experts) * capacity_factor
+    assert oracle.capacity_topk(1.25, 8 * 512, 2, 8) == 1280
+    assert oracle.capacity_topk(1.25, 1024, 1, 16) == 80  # k = 1 is the Switch capacity
+    assert oracle.capacity_topk(1.25, 10, 2, 64, 4) == 4  # min_capacity floor ([yj-zh] DeepSpeed example)
+
+
+def _literal_topk_keep(idx, E, cap, group):
+    """Flatten-order keep rule: visit (token, slot) in order; keep while the expert
+    has fewer than cap kept assignments in the current group."""
+    T, k = idx.shape
+    G = group if group > 0 else T
+    keep = np.zeros((T, k), bool)
+    for g0 in range(0, T, G):
+        used = np.zeros(E, int)
+        for t in range(g0, min(T, g0 + G)):
+            for j in range(k):
+                e = idx[t, j]
+                if used[e] < cap:
+                    keep[t, j] = True
+                    used[e] += 1
+    return keep
+
+
+@pytest.mark.parametrize("group", [0, 128])
+def test_topk_capacity_drops(group):
+    T, E, k = 512, 16, 2
+    idx = workloads.random_topk_idx(T, E, k, seed=77, skew=1.2).numpy()
+    cap = oracle.capacity_topk(1.0, group if group else T, k, E)
+    p = oracle.permute(idx, E, cap, group)
+    keep = _literal_topk_keep(idx, E, cap, group)
+    assert np.array_equal(p["slot_row"] >= 0, keep)
+    assert (~keep).any() and p["counts"].max() <= cap * (T // (group or T))
+
+
+def test_noisy_logits_reduce_to_closed_forms():
+    spec = workloads.MIXTRAL_PREFILL_BF16.replace(name="noisy", T=50, d=64, E=8, noisy=True, router_bias="normal")
+    inp = workloads.make_inputs(spec, experts=False)
+    base = oracle.logits(inp["x"], inp["wg"], inp["bg"])
+    zero = torch.zeros_like(inp["noise"])
+    assert np.array_equal(oracle.logits_noisy(inp["x"], inp["wg"], inp["bg"], inp["wn"], zero), base)
+    # Wn = 0: softplus(0) = ln 2
+    got = oracle.logits_noisy(inp["x"], inp["wg"], inp["bg"], torch.zeros_like(inp["wn"]), inp["noise"])
+    ref = base.astype(np.float64) + math.log(2.0) * inp["noise"].double().numpy()
+    assert np.allclose(got, ref, rtol=1e-6, atol=1e-6)
+
+
+def test_noisy_logits_match_torch_softplus():
+    spec = workloads.MIXTRAL_PREFILL_BF16.replace(name="noisy2", T=40, d=32, E=6, noisy=True)
+    inp = workloads.make_inputs(spec, experts=False)
+    x, wg, wn, n = (inp[k].double() for k in ("x", "wg", "wn", "noise"))
+    ref = (x @ wg.T + TF.softplus(x @ wn.T) * n).numpy()
+    got = oracle.logits_noisy(inp["x"], inp["wg"], None, inp["wn"], inp["noise"])
+    assert np.allclose(got, ref, rtol=2e-7, atol=1e-6)

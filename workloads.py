@@ -14,6 +14,8 @@ Recipe (the same for every workload):
   * DeepSeek-style layer: router bias b_e = -1.1 * ln(rank_e) with rank a seeded
     permutation of 1..E, i.e. a Zipf(1.1) prior over experts;
   * float32 draws, then rounded to bf16 (round to nearest even) for bf16 layers.
+  * noisy routers: noise projection ~ N(0, 1/d) and the standard-normal draw
+    n [T, E] are inputs like any other (seeded);
   * "integer" inputs: x in {-2..2}, router weights in {-4..4}/8 and router
     bias in {-8..8}/8, so every router product and sum is exact in float32 in
     any order and routing, ties included, can be compared bit for bit.
@@ -45,8 +47,10 @@ class LayerSpec:
     router_bias: str = "none"   # none | normal | skew | zipf
     F_shared: int = 0           # one always-on SwiGLU expert of this width; 0 = none
     capacity_factor: float = 0.0
-    capacity_group: int = 0     # Switch: tokens per capacity group (sequence length)
+    capacity_group: int = 0     # tokens per capacity group (sequence length); 0 = all tokens
     inputs: str = "gaussian"    # gaussian | integer
+    min_capacity: int = 0       # lower bound of the token-choice capacity
+    noisy: bool = False         # noisy top-k router: + softplus(x Wn^T) * n, n ~ N(0,1) given
 
     def replace(self, **kw) -> "LayerSpec":
         return dataclasses.replace(self, **kw)
@@ -145,7 +149,10 @@ def make_inputs(spec: LayerSpec, device="cpu", experts: bool = True) -> dict:
     if bg is not None and spec.inputs == "integer":
         bg = _randint((E,), -8, 8, _seed(spec, 3), device) / 8
     out = dict(x=x, wg=wg, bg=bg, w1=None, w3=None, w2=None, b1=None, b2=None,
-               ws1=None, ws3=None, ws2=None)
+               ws1=None, ws3=None, ws2=None, wn=None, noise=None)
+    if spec.noisy:
+        out["wn"] = _randn((E, d), _seed(spec, 4), device, 1.0 / math.sqrt(d)).to(dt)
+        out["noise"] = _randn((T, E), _seed(spec, 5), device)
     if not experts:
         return out
     out["w1"] = _per_expert(spec, 10, (F, d), 1.0 / math.sqrt(d), device)
