@@ -90,11 +90,18 @@ typedef struct moe_config {
     int32_t gating;          /* moe_gating */
     int32_t act;             /* moe_act */
     int32_t dtype;           /* moe_dtype of x, all weights, x_perm, y_perm and y */
-    int32_t capacity_group;  /* SWITCH: tokens per capacity group (the sequence
-                                length; a multiple of 64), 0 = all T tokens */
-    float capacity_factor;   /* SWITCH and EXPERT_CHOICE: C = int(cf * G / E) with
-                                G = capacity_group (or T) for SWITCH, T for
-                                EXPERT_CHOICE ([yj-zh] SwitchRouter) */
+    int32_t capacity_group;  /* token choice with capacity: tokens per capacity
+                                group (the sequence length; a multiple of 64),
+                                0 = all T tokens */
+    float capacity_factor;   /* SWITCH (required) and TOPK_SOFTMAX / SOFTMAX_TOPK
+                                (optional, 0 = no capacity): per group and expert
+                                C = max(min_capacity, int(cf * G * k / E)), G =
+                                capacity_group or T ([yj-zh] SwitchRouter; the
+                                [devtips] capacity example scales by top_k);
+                                assignments are kept in token order, the rest
+                                dropped.  EXPERT_CHOICE: C = int(cf * T / E). */
+    int32_t min_capacity;    /* floor of the token-choice capacity ([yj-zh]
+                                DeepSpeed MoE configuration example); 0 = none */
 } moe_config;
 
 /* Weights (device pointers). */
@@ -135,8 +142,9 @@ moe_status moe_capacity(const moe_config *cfg, int32_t *capacity);
 
 /* Workspace bytes for a stage: MOE_STAGE_FORWARD (moe_forward with routing
  * == NULL, which keeps every routing buffer and intermediate in the
- * workspace), MOE_STAGE_PERMUTE (moe_permute), MOE_STAGE_FFN (moe_expert_ffn). */
-enum { MOE_STAGE_FORWARD = 0, MOE_STAGE_PERMUTE = 1, MOE_STAGE_FFN = 2 };
+ * workspace), MOE_STAGE_PERMUTE (moe_permute), MOE_STAGE_FFN (moe_expert_ffn),
+ * MOE_STAGE_LOSSES (moe_router_losses). */
+enum { MOE_STAGE_FORWARD = 0, MOE_STAGE_PERMUTE = 1, MOE_STAGE_FFN = 2, MOE_STAGE_LOSSES = 3 };
 moe_status moe_workspace_size(const moe_config *cfg, int32_t stage, size_t *bytes);
 
 /* Router GEMM fused with gating: logits = x W_router^T + b_router (float32
@@ -148,6 +156,27 @@ moe_status moe_workspace_size(const moe_config *cfg, int32_t stage, size_t *byte
  * needs C <= 4096. */
 moe_status moe_route(const moe_config *cfg, const void *x, const moe_weights *w,
                      moe_routing *routing, void *stream);
+
+/* Noisy top-k router ([yj-ja] TopKGating, training branch; [garden]
+ * "7. 안정화 기법" Noisy Top-k): logits = x W_router^T + b_router +
+ * softplus(x W_noise^T) * noise, then the gating of cfg->gating on those
+ * logits.  w_noise: device [E][d] dtype; noise: device [T][E] float32, the
+ * standard-normal draw supplied by the caller (the library draws nothing).
+ * Token choice only; otherwise as moe_route. */
+moe_status moe_route_noisy(const moe_config *cfg, const void *x, const moe_weights *w, const void *w_noise,
+                           const float *noise, moe_routing *routing, void *stream);
+
+/* Router side outputs of token-choice gating ([yj-ja]
+ * compute_load_balancing_loss and router_z_loss; [yj-zh] load_balancing_loss):
+ *   out[0] = E * sum_e f_e * P_e  (load-balancing loss, before any weight),
+ *   out[1] = mean over tokens of logsumexp(logits_t)^2  (router z-loss),
+ *   out[2 + e] = P_e = mean over tokens of softmax(logits_t)_e,
+ * with f_e = (assignments to e in topk_idx) / (T * k), counted before any
+ * capacity drop.  logits: device [T][E] float32; topk_idx: device [T][k];
+ * out: device float [2 + E].  Deterministic fixed-order reductions.
+ * ws: MOE_STAGE_LOSSES bytes.  E <= 256; not defined for expert choice. */
+moe_status moe_router_losses(const moe_config *cfg, const float *logits, const int32_t *topk_idx, float *out,
+                             void *ws, size_t ws_bytes, void *stream);
 
 /* The gating step alone on caller-provided float32 logits [T][E] (device):
  * the same selection and weights moe_route applies after its router GEMM.

@@ -17,9 +17,10 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 GATING = {"topk_softmax": 0, "softmax_topk": 1, "switch": 2, "expert_choice": 3}
 ACT = {"relu": 0, "gelu": 1, "swiglu": 2}
 DTYPE = {"f32": 0, "bf16": 1}
-STAGE_FORWARD, STAGE_PERMUTE, STAGE_FFN = 0, 1, 2
+STAGE_FORWARD, STAGE_PERMUTE, STAGE_FFN, STAGE_LOSSES = 0, 1, 2, 3
 
-EXPORTS = ["moe_capacity", "moe_workspace_size", "moe_route", "moe_route_from_logits", "moe_permute",
+EXPORTS = ["moe_capacity", "moe_workspace_size", "moe_route", "moe_route_noisy", "moe_route_from_logits",
+           "moe_router_losses", "moe_permute",
            "moe_expert_ffn", "moe_combine", "moe_forward", "moe_last_error", "moe_timing_enable",
            "moe_timing_reset", "moe_timing_read", "moe_kernel_name"]
 
@@ -34,7 +35,8 @@ class moe_config(ctypes.Structure):
     _fields_ = [("num_tokens", ctypes.c_int32), ("d_model", ctypes.c_int32), ("num_experts", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("d_ff", ctypes.c_int32), ("d_ff_shared", ctypes.c_int32),
                 ("gating", ctypes.c_int32), ("act", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("capacity_group", ctypes.c_int32), ("capacity_factor", ctypes.c_float)]
+                ("capacity_group", ctypes.c_int32), ("capacity_factor", ctypes.c_float),
+                ("min_capacity", ctypes.c_int32)]
 
 
 class moe_weights(ctypes.Structure):
@@ -66,6 +68,8 @@ def load():
         "moe_workspace_size": [cfgp, I32, ctypes.POINTER(SZ)],
         "moe_route": [cfgp, P, ctypes.POINTER(moe_weights), ctypes.POINTER(moe_routing), P],
         "moe_route_from_logits": [cfgp, P, ctypes.POINTER(moe_routing), P],
+        "moe_route_noisy": [cfgp, P, ctypes.POINTER(moe_weights), P, P, ctypes.POINTER(moe_routing), P],
+        "moe_router_losses": [cfgp, P, P, P, P, SZ, P],
         "moe_permute": [cfgp, P, ctypes.POINTER(moe_routing), P, P, SZ, P],
         "moe_expert_ffn": [cfgp, P, P, ctypes.POINTER(moe_routing), ctypes.POINTER(moe_weights), P, P, P, SZ, P],
         "moe_combine": [cfgp, P, P, ctypes.POINTER(moe_routing), P, P],
@@ -106,16 +110,17 @@ def _stream(stream):
 # structures
 # ---------------------------------------------------------------------------
 
-def make_config(T, d, E, k, F, gating, act, dtype, F_shared=0, capacity_factor=0.0, capacity_group=0):
+def make_config(T, d, E, k, F, gating, act, dtype, F_shared=0, capacity_factor=0.0, capacity_group=0,
+                min_capacity=0):
     return moe_config(T, d, E, k, F, F_shared, GATING[gating], ACT[act], DTYPE[dtype], capacity_group,
-                      float(capacity_factor))
+                      float(capacity_factor), int(min_capacity))
 
 
 def config_from_spec(spec) -> moe_config:
     """moe_config of a layer description with attributes T, d, E, k, F, gating, act, dtype,
     F_shared, capacity_factor, capacity_group."""
     return make_config(spec.T, spec.d, spec.E, spec.k, spec.F, spec.gating, spec.act, spec.dtype,
-                       spec.F_shared, spec.capacity_factor, spec.capacity_group)
+                       spec.F_shared, spec.capacity_factor, spec.capacity_group, getattr(spec, "min_capacity", 0))
 
 
 def make_weights(t: dict) -> moe_weights:
@@ -154,6 +159,17 @@ def moe_route(cfg, x, weights: moe_weights, routing: moe_routing, stream=None):
 
 def moe_route_from_logits(cfg, logits, routing: moe_routing, stream=None):
     _check(load().moe_route_from_logits(ctypes.byref(cfg), _p(logits), ctypes.byref(routing), _stream(stream)))
+
+
+def moe_route_noisy(cfg, x, weights: moe_weights, w_noise, noise, routing: moe_routing, stream=None):
+    _check(load().moe_route_noisy(ctypes.byref(cfg), _p(x), ctypes.byref(weights), _p(w_noise), _p(noise),
+                                  ctypes.byref(routing), _stream(stream)))
+
+
+def moe_router_losses(cfg, logits, topk_idx, out, ws, stream=None):
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(load().moe_router_losses(ctypes.byref(cfg), _p(logits), _p(topk_idx), _p(out), _p(ws), nbytes,
+                                    _stream(stream)))
 
 
 def moe_permute(cfg, x, routing: moe_routing, x_perm, ws, stream=None):

@@ -293,6 +293,166 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// 4-wave variant with direct-to-LDS loads (global_load_lds_dwordx4): each
+// wave instruction moves 64 x 16 bytes straight into a contiguous 1 KB LDS
+// region, so no staging registers are needed and the accumulators of a
+// 128 x 128 wave tile (256 registers) fit.  ST LDS stages (separate LDS
+// objects) keep ST-1 K tiles in flight; one barrier per K step.
+// ---------------------------------------------------------------------------
+__device__ inline void wait_vmcnt_le(int n) {
+    // s_waitcnt with only the vector-memory counter limited (gfx9 encoding)
+    switch (n) {
+#define MOE_VMW(N) case N: __builtin_amdgcn_s_waitcnt(((N) & 15) | (((N) >> 4) << 14) | (7 << 4) | (15 << 8)); break;
+        MOE_VMW(0) MOE_VMW(8) MOE_VMW(16) MOE_VMW(24) MOE_VMW(32) MOE_VMW(40) MOE_VMW(48)
+#undef MOE_VMW
+        default: __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); break;
+    }
+}
+
+template <int BK>
+__device__ inline int swz_k(int r) { return BK == 64 ? ((r >> 1) & 7) : ((r >> 2) & 3); }
+
+template <int BM, int BN, bool GLU, int BK, int ST>
+__global__ __launch_bounds__(256) void gemm_bf16_dma_kernel(GemmParams p) {
+    constexpr int NB = GLU ? 2 * BN : BN;
+    constexpr int WTM = BM / 2, WTN = BN / 2;
+    constexpr int TM = WTM / 32, TN = WTN / 32, TB = GLU ? 2 * TN : TN;
+    constexpr int CPR = BK / 8;        // 16-byte chunks per LDS row
+    constexpr int RPI = 64 / CPR;      // rows covered by one wave instruction
+    constexpr int AI = BM / RPI / 4;   // A instructions per wave per stage
+    constexpr int BI = NB / RPI / 4;   // B instructions per wave per stage
+    constexpr int STAGE = (BM + NB) * BK;
+    constexpr int KS = BK / 16;
+    static_assert(ST >= 2 && ST <= 4, "stages");
+    static_assert(AI >= 1 && BI >= 1 && (!GLU || BN % RPI == 0), "tile");
+    __shared__ __attribute__((aligned(1024))) bf16 L0[STAGE];
+    __shared__ __attribute__((aligned(1024))) bf16 L1[STAGE];
+    __shared__ __attribute__((aligned(1024))) bf16 L2[ST > 2 ? STAGE : 8];
+    __shared__ __attribute__((aligned(1024))) bf16 L3[ST > 3 ? STAGE : 8];
+    auto stage = [&](int s) -> bf16 * { return s == 0 ? L0 : s == 1 ? L1 : s == 2 ? L2 : L3; };
+
+    const int ntn = (p.N + BN - 1) / BN;
+    const TileCoord tc = find_tile<BM>(xcd_remap(blockIdx.x), p.offsets, p.mstart, p.G, p.rows, ntn);
+    if (!tc.valid) return;
+    const int n0 = tc.nt * BN;
+    const int64_t K = p.K;
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    const int wm = wave % 2, wn = wave / 2;
+
+    const char *abase = (const char *)(p.A + tc.row0 * K);
+    const char *b0base = (const char *)(p.B0 + ((int64_t)tc.g * p.N + n0) * K);
+    const char *b1base = GLU ? (const char *)(p.B1 + ((int64_t)tc.g * p.N + n0) * K) : nullptr;
+    // per-lane byte offsets of this wave's DMA instructions (rows clamped)
+    uint32_t aoff[AI], boff[BI];
+#pragma unroll
+    for (int i = 0; i < AI; ++i) {
+        const int r = (wave * AI + i) * RPI + lane / CPR;
+        const int c = (lane % CPR) ^ swz_k<BK>(r);
+        int64_t rr = r;
+        if (tc.row0 + rr >= tc.row_end) rr = tc.row_end - 1 - tc.row0;
+        aoff[i] = (uint32_t)((rr * K + c * 8) * 2);
+    }
+#pragma unroll
+    for (int i = 0; i < BI; ++i) {
+        const int r = (wave * BI + i) * RPI + lane / CPR;  // row inside the B tile (gate rows, then up rows)
+        const int c = (lane % CPR) ^ swz_k<BK>(r);
+        int rn = (GLU && r >= BN) ? r - BN : r;
+        if (n0 + rn >= p.N) rn = p.N - 1 - n0;
+        boff[i] = (uint32_t)(((int64_t)rn * K + c * 8) * 2);
+    }
+    auto dma = [&](int kt, int s) {
+        bf16 *L = stage(s);
+        const int64_t ko = (int64_t)kt * BK * 2;
+#pragma unroll
+        for (int i = 0; i < AI; ++i)
+            __builtin_amdgcn_global_load_lds((const void *)(abase + ko + aoff[i]),
+                                             (__attribute__((address_space(3))) void *)(L + (wave * AI + i) * RPI * BK),
+                                             16, 0, 0);
+#pragma unroll
+        for (int i = 0; i < BI; ++i) {
+            const int r0 = (wave * BI + i) * RPI;
+            const char *bb = (GLU && r0 >= BN) ? b1base : b0base;
+            __builtin_amdgcn_global_load_lds((const void *)(bb + ko + boff[i]),
+                                             (__attribute__((address_space(3))) void *)(L + (BM + r0) * BK), 16, 0,
+                                             0);
+        }
+    };
+
+    f32x16 acc[TM][TB];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TB; ++j) acc[i][j] = f32x16{};
+    const int ra0 = wm * WTM + lane % 32;
+    const int rb0 = wn * WTN + lane % 32;
+    const int sa = swz_k<BK>(ra0), sb = swz_k<BK>(rb0);
+    bf16x8 fa[2][TM], fb[2][TB];
+    auto fload = [&](const bf16 *L, int ks, int slot) {
+        const int ch = ks * 2 + lane / 32;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+            fa[slot][i] = __builtin_bit_cast(bf16x8, load16(L + (ra0 + i * 32) * BK + ((ch ^ sa) * 8)));
+#pragma unroll
+        for (int j = 0; j < TB; ++j)
+            fb[slot][j] = __builtin_bit_cast(
+                bf16x8, load16(L + (BM + (j >= TN ? BN : 0) + rb0 + (j % TN) * 32) * BK + ((ch ^ sb) * 8)));
+    };
+    auto compute = [&](const bf16 *L) {
+        fload(L, 0, 0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if (ks + 1 < KS) fload(L, ks + 1, (ks + 1) & 1);
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TB; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks & 1][i], fb[ks & 1][j], acc[i][j],
+                                                                        0, 0, 0);
+        }
+    };
+
+    const int KT = p.K / BK;
+#pragma unroll
+    for (int s = 0; s < ST - 1; ++s) dma(min(s, KT - 1), s);
+    // step k: wait for this wave's DMA of tile k, barrier (all DMAs of tile k
+    // landed, every wave done with stage (k-1) % ST), refill that stage with
+    // tile k+ST-1, compute tile k.  Unrolled by ST so stages are static.
+    for (int k0 = 0; k0 < KT; k0 += ST) {
+#pragma unroll
+        for (int u = 0; u < ST; ++u) {
+            const int k = k0 + u;
+            if (k < KT) {
+                wait_vmcnt_le((ST - 2) * (AI + BI));
+                __syncthreads();
+                dma(min(k + ST - 1, KT - 1), (u + ST - 1) % ST);
+                compute(stage(u));
+            }
+        }
+    }
+
+    const float *bias = p.bias ? p.bias + (int64_t)tc.g * p.N : nullptr;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int col = n0 + wn * WTN + j * 32 + lane % 32;
+            if (col >= p.N) continue;
+            const float bcol = bias ? bias[col] : 0.f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int64_t row = tc.row0 + wm * WTM + i * 32 + 8 * q + 4 * (lane / 32) + jj;
+                    if (row >= tc.row_end) continue;
+                    float v = acc[i][j][4 * q + jj];
+                    if constexpr (GLU) v = silu(v) * acc[i][TN + j][4 * q + jj];
+                    else v = apply_act(p.act, v + bcol);
+                    p.C[row * p.N + col] = (bf16)v;
+                }
+        }
+}
+
+// ---------------------------------------------------------------------------
 // float32 grouped GEMM on the vector ALUs: 64x64 tiles, 4x4 outputs per
 // thread, K in steps of 16 through LDS.
 // ---------------------------------------------------------------------------

@@ -22,10 +22,15 @@ struct RouteArgs {
     float *logits;  // may be null for token choice
     int32_t *idx;
     float *w;
+    const void *wn;       // noisy router: noise projection [E][d], else null
+    const float *noise;   // noisy router: [T][E] standard-normal draw, else null
 };
 void launch_route(const RouteArgs &a, hipStream_t s);
 void launch_gate_logits(const float *logits, int T, int E, int k, int gating, int32_t *idx, float *w,
                         hipStream_t s);
+constexpr int kStatTokens = 256;  // tokens per block of the router statistics
+void launch_router_stats(const float *logits, const int32_t *idx, int T, int E, int k, float *part,
+                         int32_t *cnt, float *out, hipStream_t s);
 void launch_ec_select(const float *logits, int T, int E, int C, int32_t *ec_idx, float *ec_score,
                       hipStream_t s);
 

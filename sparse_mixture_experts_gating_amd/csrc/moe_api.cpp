@@ -34,11 +34,11 @@ moe_status fail(moe_status st, const char *fmt, ...) {
 // ---------------------------------------------------------------------------
 enum Kind {
     K_ROUTE, K_GATE_LOGITS, K_EC_SELECT, K_PERM_COUNT, K_PERM_SCAN, K_PERM_SCATTER, K_EC_PERMUTE, K_GATHER,
-    K_TILE_PLAN, K_GEMM1, K_GEMM2, K_GEMM1_SHARED, K_GEMM2_SHARED, K_COMBINE, K_COUNT
+    K_TILE_PLAN, K_GEMM1, K_GEMM2, K_GEMM1_SHARED, K_GEMM2_SHARED, K_COMBINE, K_ROUTER_STATS, K_COUNT
 };
 const char *kKindNames[K_COUNT] = {"route", "gate_logits", "ec_select", "permute_count", "permute_scan",
                                    "permute_scatter", "ec_permute", "gather_rows", "tile_plan", "gemm1_act",
-                                   "gemm2", "gemm1_act_shared", "gemm2_shared", "combine"};
+                                   "gemm2", "gemm1_act_shared", "gemm2_shared", "combine", "router_stats"};
 
 struct Pending {
     hipEvent_t a, b;
@@ -104,10 +104,16 @@ struct Derived {
     size_t elem;       // bytes per element of dtype
 };
 
+bool token_choice_capacity(const moe_config *c) {
+    return c->gating == MOE_GATE_SWITCH ||
+           ((c->gating == MOE_GATE_TOPK_SOFTMAX || c->gating == MOE_GATE_SOFTMAX_TOPK) && c->capacity_factor > 0.f);
+}
+
 int capacity_of(const moe_config *c) {
-    if (c->gating == MOE_GATE_SWITCH) {
+    if (token_choice_capacity(c)) {
         const double G = c->capacity_group > 0 ? (double)c->capacity_group : (double)c->num_tokens;
-        return (int)((double)c->capacity_factor * G / (double)c->num_experts);
+        const int cap = (int)((double)c->capacity_factor * G * (double)c->top_k / (double)c->num_experts);
+        return cap < c->min_capacity ? c->min_capacity : cap;
     }
     if (c->gating == MOE_GATE_EXPERT_CHOICE)
         return (int)((double)c->capacity_factor * (double)c->num_tokens / (double)c->num_experts);
@@ -138,9 +144,12 @@ moe_status derive(const moe_config *c, Derived *o) {
         return fail(MOE_ERR_INVALID_ARG, "top_k %d outside [1, num_experts=%d]", c->top_k, c->num_experts);
     o->capacity = 0;
     o->group_chunks = 0;
-    if (c->gating == MOE_GATE_SWITCH) {
-        if (c->top_k != 1) return fail(MOE_ERR_INVALID_ARG, "Switch gating needs top_k == 1");
-        if (!(c->capacity_factor > 0.f)) return fail(MOE_ERR_INVALID_ARG, "Switch gating needs capacity_factor > 0");
+    if (c->min_capacity < 0) return fail(MOE_ERR_INVALID_ARG, "min_capacity < 0");
+    if (c->capacity_factor < 0.f) return fail(MOE_ERR_INVALID_ARG, "capacity_factor < 0");
+    if (c->gating == MOE_GATE_SWITCH && c->top_k != 1) return fail(MOE_ERR_INVALID_ARG, "Switch gating needs top_k == 1");
+    if (c->gating == MOE_GATE_SWITCH && !(c->capacity_factor > 0.f))
+        return fail(MOE_ERR_INVALID_ARG, "Switch gating needs capacity_factor > 0");
+    if (token_choice_capacity(c)) {
         if (c->capacity_group < 0) return fail(MOE_ERR_INVALID_ARG, "capacity_group < 0");
         if (c->capacity_group % kChunk != 0)
             return fail(MOE_ERR_UNSUPPORTED, "capacity_group %d is not a multiple of %d", c->capacity_group, kChunk);
@@ -194,6 +203,17 @@ PermuteWs carve_permute(const Derived &D, Carve &c) {
     w.pre = c.take(ce);
     w.base = c.take(ce);
     w.ranks = c.take((size_t)D.T * D.k * 4);
+    return w;
+}
+
+struct LossWs {
+    size_t part, cnt;
+};
+LossWs carve_losses(const Derived &D, Carve &c) {
+    const int64_t nb = (D.T + kStatTokens - 1) / kStatTokens;
+    LossWs w{};
+    w.part = c.take((size_t)nb * (D.E + 1) * 4);
+    w.cnt = c.take((size_t)nb * D.E * 4);
     return w;
 }
 
@@ -257,10 +277,11 @@ moe_status check_weights_ffn(const Derived &D, const moe_weights *w) {
 // ---------------------------------------------------------------------------
 // stage bodies (arguments already checked)
 // ---------------------------------------------------------------------------
-moe_status do_route(const Derived &D, const void *x, const moe_weights *w, const moe_routing *r, hipStream_t s) {
+moe_status do_route(const Derived &D, const void *x, const moe_weights *w, const moe_routing *r, hipStream_t s,
+                    const void *w_noise = nullptr, const float *noise = nullptr) {
     if (D.T == 0) return MOE_OK;
     RouteArgs a{x, w->w_router, w->b_router, (int)D.T, (int)D.d, (int)D.E, (int)D.k, D.gating, D.bf16,
-                r->logits, r->topk_idx, r->topk_w};
+                r->logits, r->topk_idx, r->topk_w, w_noise, noise};
     TRY(launch(K_ROUTE, s, [&] { launch_route(a, s); }));
     if (D.ec)
         TRY(launch(K_EC_SELECT, s, [&] {
@@ -295,7 +316,7 @@ int pick_shape(const Derived &D) {
     if (D.ec) return D.capacity <= 160 ? kGemmSmallM : kGemmPrefill;
     if (D.T <= 32) return kGemmDecode;
     int64_t max_rows = D.T;
-    if (D.gating == MOE_GATE_SWITCH) {
+    if (D.capacity > 0) {
         const int64_t groups = D.group_chunks ? (D.T + D.group_chunks * kChunk - 1) / (D.group_chunks * kChunk) : 1;
         max_rows = std::min<int64_t>(D.T, groups * D.capacity);
     }
@@ -383,6 +404,7 @@ moe_status moe_workspace_size(const moe_config *cfg, int32_t stage, size_t *byte
     if (stage == MOE_STAGE_FORWARD) carve_forward(D, c);
     else if (stage == MOE_STAGE_PERMUTE) carve_permute(D, c);
     else if (stage == MOE_STAGE_FFN) carve_ffn(D, c);
+    else if (stage == MOE_STAGE_LOSSES) carve_losses(D, c);
     else return fail(MOE_ERR_INVALID_ARG, "unknown stage %d", stage);
     *bytes = c.off;
     return MOE_OK;
@@ -401,6 +423,46 @@ moe_status moe_route(const moe_config *cfg, const void *x, const moe_weights *w,
     TRY(check_routing(D, routing, false));
     if (D.ec) TRY(need_ptr(routing->logits, "routing.logits (required for expert choice)", false));
     return do_route(D, x, w, routing, (hipStream_t)stream);
+}
+
+moe_status moe_route_noisy(const moe_config *cfg, const void *x, const moe_weights *w, const void *w_noise,
+                           const float *noise, moe_routing *routing, void *stream) {
+    g_err.clear();
+    Derived D;
+    TRY(derive(cfg, &D));
+    if (D.T == 0) return MOE_OK;  // empty batch: nothing to launch
+    if (D.ec) return fail(MOE_ERR_UNSUPPORTED, "the noisy router is defined for token-choice gating");
+    TRY(check_route_limits(D));
+    TRY(need_ptr(x, "x"));
+    if (!w) return fail(MOE_ERR_INVALID_ARG, "weights is NULL");
+    TRY(need_ptr(w->w_router, "w_router"));
+    TRY(need_ptr(w_noise, "w_noise"));
+    TRY(need_ptr(noise, "noise", false));
+    TRY(check_routing(D, routing, false));
+    return do_route(D, x, w, routing, (hipStream_t)stream, w_noise, noise);
+}
+
+moe_status moe_router_losses(const moe_config *cfg, const float *logits, const int32_t *topk_idx, float *out,
+                             void *ws, size_t ws_bytes, void *stream) {
+    g_err.clear();
+    Derived D;
+    TRY(derive(cfg, &D));
+    if (D.ec) return fail(MOE_ERR_UNSUPPORTED, "router losses are defined for token-choice gating");
+    if (D.E > 256) return fail(MOE_ERR_UNSUPPORTED, "router losses handle at most 256 experts");
+    if (D.T == 0) return fail(MOE_ERR_INVALID_ARG, "router losses need at least one token");
+    TRY(need_ptr(logits, "logits", false));
+    TRY(need_ptr(topk_idx, "topk_idx", false));
+    TRY(need_ptr(out, "out", false));
+    Carve c;
+    const LossWs lw = carve_losses(D, c);
+    TRY(need_ptr(ws, "ws"));
+    if (ws_bytes < c.off) return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, c.off);
+    hipStream_t s = (hipStream_t)stream;
+    char *base = (char *)ws;
+    return launch(K_ROUTER_STATS, s, [&] {
+        launch_router_stats(logits, topk_idx, (int)D.T, (int)D.E, (int)D.k, (float *)(base + lw.part),
+                            (int32_t *)(base + lw.cnt), out, s);
+    });
 }
 
 moe_status moe_route_from_logits(const moe_config *cfg, const float *logits, moe_routing *routing, void *stream) {

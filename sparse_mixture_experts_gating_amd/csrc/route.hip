@@ -84,16 +84,22 @@ __device__ void gate_one_token(const float *row, int E, int k, int gating, int64
 // range, straight from global memory (x rows are read once; the router
 // weights stay in L1/L2).  Partial sums meet in LDS in a fixed order, the
 // bias is added, logits are written, and each wave gates whole tokens.
-template <int WM, int NT>
+__device__ inline float softplus(float u) { return fmaxf(u, 0.f) + log1pf(expf(-fabsf(u))); }
+
+// NOISY adds the noise projection as a second MFMA accumulator set and forms
+// x.Wg + b + softplus(x.Wn) * noise ([yj-ja] TopKGating, training branch).
+template <int WM, int NT, bool NOISY>
 __global__ __launch_bounds__(256) void route_bf16_kernel(
     const bf16 *__restrict__ x, const bf16 *__restrict__ wg, const float *__restrict__ bias,
     int T, int d, int E, int k, int gating, float *__restrict__ logits,
-    int32_t *__restrict__ idx_out, float *__restrict__ w_out) {
+    int32_t *__restrict__ idx_out, float *__restrict__ w_out, const bf16 *__restrict__ wn,
+    const float *__restrict__ noise) {
     constexpr int WK = 4 / WM;
     constexpr int TOK = 16 * WM;
     constexpr int EP = 16 * NT;
     constexpr int LD = EP + 4;
     __shared__ float part[WK * TOK * LD];
+    __shared__ float partn[NOISY ? WK * TOK * LD : 1];
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int wm = wave % WM, wk = wave / WM;
     const int64_t tok0 = (int64_t)blockIdx.x * TOK;
@@ -102,15 +108,20 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(
     if (trow >= T) trow = T - 1;
     const bf16 *xa = x + trow * d + kq;
     const bf16 *wb[NT];
+    int64_t woff[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         int e = nt * 16 + r;
         if (e >= E) e = E - 1;
-        wb[nt] = wg + (int64_t)e * d + kq;
+        woff[nt] = (int64_t)e * d + kq;
+        wb[nt] = wg + woff[nt];
     }
-    f32x4 acc[NT];
+    f32x4 acc[NT], accn[NOISY ? NT : 1];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int nt = 0; nt < NT; ++nt) {
+        acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (NOISY) accn[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     const int nk = d / 32;
     const int kb = nk * wk / WK, ke = nk * (wk + 1) / WK;
     for (int kc = kb; kc < ke; ++kc) {
@@ -119,14 +130,20 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(
         for (int nt = 0; nt < NT; ++nt) {
             const bf16x8 b = __builtin_bit_cast(bf16x8, load16(wb[nt] + kc * 32));
             acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[nt], 0, 0, 0);
+            if constexpr (NOISY) {
+                const bf16x8 bn = __builtin_bit_cast(bf16x8, load16(wn + woff[nt] + kc * 32));
+                accn[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bn, accn[nt], 0, 0, 0);
+            }
         }
     }
     // D[row = 4*(lane/16) + j][col = lane%16] of each 16x16 tile
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 4; ++j) {
             part[(wk * TOK + wm * 16 + 4 * (lane / 16) + j) * LD + nt * 16 + r] = acc[nt][j];
+            if constexpr (NOISY) partn[(wk * TOK + wm * 16 + 4 * (lane / 16) + j) * LD + nt * 16 + r] = accn[nt][j];
+        }
     __syncthreads();
     for (int i = threadIdx.x; i < TOK * EP; i += 256) {
         const int tt = i / EP, e = i % EP;
@@ -135,6 +152,13 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(
         for (int w = 1; w < WK; ++w) s += part[(w * TOK + tt) * LD + e];
         if (e < E) {
             if (bias) s += bias[e];
+            if constexpr (NOISY) {
+                float u = partn[tt * LD + e];
+#pragma unroll
+                for (int w = 1; w < WK; ++w) u += partn[(w * TOK + tt) * LD + e];
+                const int64_t t = tok0 + tt < T ? tok0 + tt : T - 1;
+                s += softplus(u) * noise[t * E + e];
+            }
             if (logits && tok0 + tt < T) logits[(tok0 + tt) * E + e] = s;
         }
         part[tt * LD + e] = s;
@@ -151,7 +175,8 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(
 __global__ __launch_bounds__(256) void route_f32_kernel(
     const float *__restrict__ x, const float *__restrict__ wg, const float *__restrict__ bias,
     int T, int d, int E, int k, int gating, float *__restrict__ logits,
-    int32_t *__restrict__ idx_out, float *__restrict__ w_out) {
+    int32_t *__restrict__ idx_out, float *__restrict__ w_out, const float *__restrict__ wn,
+    const float *__restrict__ noise) {
     __shared__ float rows[4][256];
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int64_t t = (int64_t)blockIdx.x * 4 + wave;
@@ -163,6 +188,12 @@ __global__ __launch_bounds__(256) void route_f32_kernel(
             float s = 0.f;
             for (int i = 0; i < d; ++i) s = fmaf(xr[i], wr[i], s);
             if (bias) s += bias[e];
+            if (wn) {
+                const float *nr = wn + (int64_t)e * d;
+                float u = 0.f;
+                for (int i = 0; i < d; ++i) u = fmaf(xr[i], nr[i], u);
+                s += softplus(u) * noise[t * E + e];
+            }
             rows[wave][e] = s;
             if (logits) logits[t * E + e] = s;
         }
@@ -178,6 +209,105 @@ __global__ __launch_bounds__(256) void gate_logits_kernel(const float *__restric
     const int wave = threadIdx.x / kWave;
     const int64_t t = (int64_t)blockIdx.x * 4 + wave;
     if (t < T) gate_one_token(logits + t * E, E, k, gating, t, idx_out, w_out);
+}
+
+// ---------------------------------------------------------------------------
+// Router statistics ([yj-ja] compute_load_balancing_loss, router_z_loss):
+// each block owns kStatTokens consecutive tokens; each wave walks its tokens
+// in order accumulating softmax probabilities (lane l: experts l + 64q),
+// logsumexp^2 and selection counts; the waves' partials meet in LDS in wave
+// order.  A one-block pass then sums the block partials in block order.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void router_stats_kernel(const float *__restrict__ logits,
+                                                           const int32_t *__restrict__ idx, int T, int E, int k,
+                                                           float *__restrict__ part, int32_t *__restrict__ cnt) {
+    __shared__ float sp[4][257];
+    __shared__ int sc[4][256];
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    float pacc[4] = {0.f, 0.f, 0.f, 0.f};
+    int cacc[4] = {0, 0, 0, 0};
+    float zacc = 0.f;
+    for (int tt = wave; tt < kStatTokens; tt += 4) {
+        const int64_t t = (int64_t)blockIdx.x * kStatTokens + tt;
+        if (t >= T) break;
+        const float *row = logits + t * E;
+        float v[4];
+        float m = -INFINITY;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = lane + kWave * q;
+            v[q] = e < E ? row[e] : -INFINITY;
+            m = fmaxf(m, v[q]);
+        }
+        m = wave_max(m);
+        float ex[4], s = 0.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            ex[q] = lane + kWave * q < E ? expf(v[q] - m) : 0.f;
+            s += ex[q];
+        }
+        s = wave_sum(s);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) pacc[q] += ex[q] / s;
+        const float lse = m + logf(s);
+        zacc += lse * lse;
+        for (int j = 0; j < k; ++j) {
+            const int e = idx[t * k + j];
+            if (e >= 0 && e < E && lane == (e & (kWave - 1))) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if ((e >> 6) == q) ++cacc[q];
+            }
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        sp[wave][lane + kWave * q] = pacc[q];
+        sc[wave][lane + kWave * q] = cacc[q];
+    }
+    if (lane == 0) sp[wave][256] = zacc;
+    __syncthreads();
+    const int e = threadIdx.x;
+    float* pb = part + (int64_t)blockIdx.x * (E + 1);
+    if (e < E) {
+        pb[e] = ((sp[0][e] + sp[1][e]) + sp[2][e]) + sp[3][e];
+        cnt[(int64_t)blockIdx.x * E + e] = sc[0][e] + sc[1][e] + sc[2][e] + sc[3][e];
+    }
+    if (e == 0) pb[E] = ((sp[0][256] + sp[1][256]) + sp[2][256]) + sp[3][256];
+}
+
+__global__ __launch_bounds__(256) void router_stats_finalize_kernel(const float *__restrict__ part,
+                                                                    const int32_t *__restrict__ cnt, int nb, int T,
+                                                                    int E, int k, float *__restrict__ out) {
+    __shared__ float prod[256];
+    const int e = threadIdx.x;
+    if (e < E) {
+        float ps = 0.f;
+        int64_t cs = 0;
+        for (int b = 0; b < nb; ++b) {
+            ps += part[(int64_t)b * (E + 1) + e];
+            cs += cnt[(int64_t)b * E + e];
+        }
+        const float P = ps / (float)T;
+        const float f = (float)((double)cs / ((double)T * k));
+        out[2 + e] = P;
+        prod[e] = f * P;
+    }
+    __syncthreads();
+    if (e == 0) {
+        float a = 0.f, z = 0.f;
+        for (int i = 0; i < E; ++i) a += prod[i];
+        for (int b = 0; b < nb; ++b) z += part[(int64_t)b * (E + 1) + E];
+        out[0] = (float)E * a;
+        out[1] = z / (float)T;
+    }
+}
+
+void launch_router_stats(const float *logits, const int32_t *idx, int T, int E, int k, float *part, int32_t *cnt,
+                         float *out, hipStream_t s) {
+    const int nb = (T + kStatTokens - 1) / kStatTokens;
+    hipLaunchKernelGGL(router_stats_kernel, dim3(nb), dim3(256), 0, s, logits, idx, T, E, k, part, cnt);
+    hipLaunchKernelGGL(router_stats_finalize_kernel, dim3(1), dim3(256), 0, s, part, cnt, nb, T, E, k, out);
 }
 
 // ---------------------------------------------------------------------------
@@ -339,15 +469,22 @@ template <int WM, int NT>
 static void launch_route_bf16_t(const RouteArgs &a, hipStream_t s) {
     const int tok = 16 * WM;
     const int grid = (a.T + tok - 1) / tok;
-    hipLaunchKernelGGL((route_bf16_kernel<WM, NT>), dim3(grid), dim3(256), 0, s, (const bf16 *)a.x,
-                       (const bf16 *)a.wg, a.bias, a.T, a.d, a.E, a.k, a.gating, a.logits, a.idx, a.w);
+    if (a.wn)
+        hipLaunchKernelGGL((route_bf16_kernel<WM, NT, true>), dim3(grid), dim3(256), 0, s, (const bf16 *)a.x,
+                           (const bf16 *)a.wg, a.bias, a.T, a.d, a.E, a.k, a.gating, a.logits, a.idx, a.w,
+                           (const bf16 *)a.wn, a.noise);
+    else
+        hipLaunchKernelGGL((route_bf16_kernel<WM, NT, false>), dim3(grid), dim3(256), 0, s, (const bf16 *)a.x,
+                           (const bf16 *)a.wg, a.bias, a.T, a.d, a.E, a.k, a.gating, a.logits, a.idx, a.w,
+                           nullptr, nullptr);
 }
 
 void launch_route(const RouteArgs &a, hipStream_t s) {
     if (a.T == 0) return;
     if (!a.bf16) {
         hipLaunchKernelGGL(route_f32_kernel, dim3((a.T + 3) / 4), dim3(256), 0, s, (const float *)a.x,
-                           (const float *)a.wg, a.bias, a.T, a.d, a.E, a.k, a.gating, a.logits, a.idx, a.w);
+                           (const float *)a.wg, a.bias, a.T, a.d, a.E, a.k, a.gating, a.logits, a.idx, a.w,
+                           (const float *)a.wn, a.noise);
         return;
     }
     if (a.E <= 16) launch_route_bf16_t<1, 1>(a, s);
