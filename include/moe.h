@@ -30,6 +30,10 @@
  *   - Layouts are row-major; weights follow nn.Linear ([out][in]), stacked
  *     over experts.  dtype MOE_BF16 means bfloat16 storage with float32
  *     accumulation; MOE_F32 is float32 throughout.
+ *   - Supported shapes (else MOE_ERR_UNSUPPORTED): d_model, d_ff and
+ *     d_ff_shared multiples of 64 (bf16) or 16 (f32) and at most 2^21;
+ *     num_experts <= 1024, and <= 256 for the fused router and the router
+ *     losses; expert-choice capacity <= 4096; T * k < 2^31.
  */
 #ifndef MOE_H
 #define MOE_H

@@ -14,6 +14,8 @@
 // Me m-tiles, tiles run in groups of Me x gN (m fastest, gN ~ 32 / Me weight
 // panels), and every XCD receives runs of 32 consecutive tiles: a run shares
 // the expert's activation tiles and a few weight panels in that XCD's L2.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -82,6 +84,17 @@ __device__ inline TileCoord find_tile(int tile, const int32_t *offsets, const in
     return c;
 }
 
+// Raw buffer resource over `bytes` bytes from `base` (limit clamped to 2^31 - 1;
+// callers address at most a 256-row tile from the base).  Loads at offsets
+// at or past the limit return zeros.
+__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, int64_t bytes) {
+    const int64_t lim = bytes < 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)lim, 0x00020000);
+}
+__device__ inline u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, soff, 0));
+}
+
 // LDS tiles hold rows of 64 bf16 (128 bytes = eight 16-byte chunks).  Chunk c
 // of row r is stored at chunk slot c ^ swz(r) so that the 16-byte reads of 16
 // consecutive rows at one chunk index touch distinct banks.
@@ -99,12 +112,57 @@ struct GemmParams {
     int64_t rows;
     int N, K;
     int act;
+    // split K of the last, partial round of tiles (null part: off)
+    float *part;      // [slots][BM * NB] float32 partial accumulators
+    int32_t *cnt;     // [slots] arrival counters, zero between launches
+    int slots;        // workgroups resident at once (one per CU)
+    int max_split;    // at most this many K parts per tile
 };
+
+// Work item of one workgroup.  The tiles fill rounds of `slots` workgroups;
+// when the last round is partial (rem tiles), each of its tiles is split into
+// S = slots / rem parts along K, so that the last round is as wide as the
+// others and each part runs 1/S of the K loop.  The parts of a tile are
+// consecutive logical indices inside one run of 32, i.e. on one XCD.
+struct WorkItem {
+    int tile;    // logical tile
+    int part;    // K part (0 when not split)
+    int S;       // K parts of this tile
+    int unit;    // index of the split tile among the split ones (S > 1)
+    bool valid;
+};
+
+__device__ inline WorkItem work_item(int w, int ntiles, const GemmParams &p) {
+    WorkItem it{w, 0, 1, 0, w < ntiles};
+    if (p.part == nullptr || ntiles <= 0) return it;
+    const int rem = ntiles % p.slots;
+    if (rem == 0) return it;
+    int S = min(p.slots / rem, p.max_split);
+    S = S > 1 ? 1 << (31 - __clz(S)) : 1;  // a power of two: the parts stay inside one 32-tile XCD run
+    if (S < 2) return it;
+    const int full = ntiles - rem;
+    if (w < full) return it;
+    const int u = w - full;
+    it.valid = u < rem * S;
+    it.unit = u / S;
+    it.tile = full + it.unit;
+    it.part = u % S;
+    it.S = S;
+    return it;
+}
+
+__device__ inline int total_tiles(int BM, int ntn, const int32_t *offsets, const int32_t *mstart, int G,
+                                  int64_t rows) {
+    if (offsets == nullptr) return (int)((rows + BM - 1) / BM) * ntn;
+    return mstart[G] * ntn;
+}
 
 // PD: K tiles in flight in registers (1: one set, loads issued a step ahead;
 // 2: two sets, loads issued two steps ahead).  SB: pin the loads at the head
 // of each step (scheduling barrier).  FB: double-buffer MFMA fragments.
-template <int BM, int BN, int WM, int WN, bool GLU, bool FB, int PD = 2, bool SB = true>
+// IL: 0 = compiler schedule; 1 = the next substep's LDS reads interleaved
+// 1:1 with this substep's MFMAs; 2 = all next-substep reads first, then the MFMAs.
+template <int BM, int BN, int WM, int WN, bool GLU, bool FB, int PD = 2, bool SB = true, int IL = 0>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
     constexpr int NT = 64 * WM * WN;  // threads
     constexpr int BK = 64;
@@ -119,36 +177,47 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
     static_assert(!GLU || BN % RSTEP == 0, "gate/up split must fall between a thread's chunks");
     static_assert(TM >= 1 && TN >= 1, "wave tile");
     __shared__ __attribute__((aligned(16))) bf16 lds[2][(BM + NB) * BK];
+    __shared__ int last_part;
 
     const int ntn = (p.N + BN - 1) / BN;
-    const TileCoord tc = find_tile<BM>(xcd_remap(blockIdx.x), p.offsets, p.mstart, p.G, p.rows, ntn);
+    const WorkItem wi = work_item(xcd_remap(blockIdx.x),
+                                  total_tiles(BM, ntn, p.offsets, p.mstart, p.G, p.rows), p);
+    if (!wi.valid) return;
+    const TileCoord tc = find_tile<BM>(wi.tile, p.offsets, p.mstart, p.G, p.rows, ntn);
     if (!tc.valid) return;
     const int n0 = tc.nt * BN;
     const int64_t K = p.K;
+    // K tiles [kbeg, kbeg + KT) of this work item
+    const int KT_all = p.K / BK;
+    const int kbeg = (int)((int64_t)KT_all * wi.part / wi.S);
+    const int KT = (int)((int64_t)KT_all * (wi.part + 1) / wi.S) - kbeg;
 
     const int tid = threadIdx.x;
     const int wave = tid / kWave, lane = tid % kWave;
     const int wm = wave % WM, wn = wave / WM;
 
-    // Loads: uniform tile bases plus 32-bit per-chunk byte offsets (rows
-    // clamped into the group / matrix).  Thread tid moves chunk (tid % 8) of
-    // rows tid/8 + RSTEP*i.
+    // Loads: buffer loads from uniform tile bases with 32-bit per-chunk byte
+    // offsets; the K offset goes in the scalar offset.  The byte limit of
+    // each buffer ends at the expert's last row (A) or the matrix's last row
+    // (B), so rows past it read as zeros: padding rows of a partial tile feed
+    // the MFMAs zeros rather than copies of real rows, which keeps their
+    // switching power low.  Thread tid moves chunk (tid % 8) of rows
+    // tid/8 + RSTEP*i.
     const int r0 = tid / 8, ch0 = tid % 8;
-    const char *abase = (const char *)(p.A + tc.row0 * K);
-    const char *b0base = (const char *)(p.B0 + ((int64_t)tc.g * p.N + n0) * K);
-    const char *b1base = GLU ? (const char *)(p.B1 + ((int64_t)tc.g * p.N + n0) * K) : nullptr;
+    const int64_t k0 = (int64_t)kbeg * BK;
+    const char *abase = (const char *)(p.A + tc.row0 * K + k0);
+    const char *b0base = (const char *)(p.B0 + ((int64_t)tc.g * p.N + n0) * K + k0);
+    const char *b1base = GLU ? (const char *)(p.B1 + ((int64_t)tc.g * p.N + n0) * K + k0) : nullptr;
+    const __amdgpu_buffer_rsrc_t arsrc = buffer_rsrc(abase, (tc.row_end - tc.row0) * K * 2);
+    const __amdgpu_buffer_rsrc_t b0rsrc = buffer_rsrc(b0base, (int64_t)(p.N - n0) * K * 2);
+    const __amdgpu_buffer_rsrc_t b1rsrc = GLU ? buffer_rsrc(b1base, (int64_t)(p.N - n0) * K * 2) : b0rsrc;
     uint32_t aoff[A_PER_T], boff[B_PER_T];
 #pragma unroll
-    for (int i = 0; i < A_PER_T; ++i) {
-        int64_t r = r0 + RSTEP * i;
-        if (tc.row0 + r >= tc.row_end) r = tc.row_end - 1 - tc.row0;
-        aoff[i] = (uint32_t)((r * K + ch0 * 8) * 2);
-    }
+    for (int i = 0; i < A_PER_T; ++i) aoff[i] = (uint32_t)(((r0 + RSTEP * i) * K + ch0 * 8) * 2);
 #pragma unroll
     for (int i = 0; i < B_PER_T; ++i) {
         int r = r0 + RSTEP * i;
         if (GLU && r >= BN) r -= BN;
-        if (n0 + r >= p.N) r = p.N - 1 - n0;
         boff[i] = (uint32_t)(((int64_t)r * K + ch0 * 8) * 2);
     }
     // LDS: chunk c of row r sits at chunk slot c ^ swz(r); swz is the same for
@@ -171,14 +240,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
     // MFMAs consume one, the next tile is stored into the other.
     u32x4 ra[2][A_PER_T], rb[2][B_PER_T];
     auto gload = [&](int kt, int set) {
-        const int64_t ko = (int64_t)kt * BK * 2;
-        const char *ab = abase + ko, *b0 = b0base + ko, *b1 = GLU ? b1base + ko : nullptr;
+        const int ko = kt * BK * 2;
 #pragma unroll
-        for (int i = 0; i < A_PER_T; ++i) ra[set][i] = load16(ab + aoff[i]);
+        for (int i = 0; i < A_PER_T; ++i) ra[set][i] = buffer_load16(arsrc, aoff[i], ko);
 #pragma unroll
         for (int i = 0; i < B_PER_T; ++i) {
             const bool up = GLU && RSTEP * i >= BN;
-            rb[set][i] = load16((up ? b1 : b0) + boff[i]);
+            rb[set][i] = buffer_load16(up ? b1rsrc : b0rsrc, boff[i], ko);
         }
     };
     auto lstore = [&](int buf, int set) {
@@ -214,6 +282,20 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
             if constexpr (FB) {
                 if (ks + 1 < BK / 16) fload(L, ks + 1, (ks + 1) & 1);
                 mfmas(ks & 1);
+                if constexpr (IL == 1) {
+                    if (ks + 1 < BK / 16) {
+#pragma unroll
+                        for (int g = 0; g < TM + TB; ++g) {
+                            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        }
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                } else if constexpr (IL == 2) {
+                    if (ks + 1 < BK / 16) __builtin_amdgcn_sched_group_barrier(0x100, TM + TB, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, TM * TB, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             } else {
                 if (ks > 0) fload(L, ks, 0);
                 mfmas(0);
@@ -221,7 +303,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
         }
     };
 
-    const int KT = p.K / BK;
     if constexpr (PD == 1) {
         // one register set: tile kt+1 is loaded during step kt and stored into
         // the other LDS buffer at its end (the tail re-reads tile KT-1)
@@ -269,6 +350,46 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
         }
     }
 
+    if (wi.S > 1) {
+        // Publish this part's accumulators; the last part to arrive adds the
+        // S parts in part order (the sum does not depend on arrival order)
+        // and runs the epilogue.  Layout: 16-byte chunk q4 of acc[i][j] of
+        // thread tid at ((i * TB + j) * 4 + q4) * NT + tid.
+        constexpr int PER_UNIT = BM * NB;
+        float *mine = p.part + ((int64_t)wi.unit * wi.S + wi.part) * PER_UNIT;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TB; ++j)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    f32x4 v = {acc[i][j][4 * q4], acc[i][j][4 * q4 + 1], acc[i][j][4 * q4 + 2], acc[i][j][4 * q4 + 3]};
+                    *(f32x4 *)(mine + (((i * TB + j) * 4 + q4) * NT + tid) * 4) = v;
+                }
+        __threadfence();
+        __syncthreads();
+        if (tid == 0) last_part = atomicAdd(p.cnt + wi.unit, 1) == wi.S - 1;
+        __syncthreads();
+        if (!last_part) return;
+        __threadfence();
+        const float *parts = p.part + (int64_t)wi.unit * wi.S * PER_UNIT;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TB; ++j)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int64_t o = (((i * TB + j) * 4 + q4) * NT + tid) * 4;
+                    f32x4 v = *(const f32x4 *)(parts + o);
+                    for (int sp = 1; sp < wi.S; ++sp) v += *(const f32x4 *)(parts + (int64_t)sp * PER_UNIT + o);
+                    acc[i][j][4 * q4] = v[0];
+                    acc[i][j][4 * q4 + 1] = v[1];
+                    acc[i][j][4 * q4 + 2] = v[2];
+                    acc[i][j][4 * q4 + 3] = v[3];
+                }
+        if (tid == 0) p.cnt[wi.unit] = 0;  // ready for the next launch
+    }
+
     // epilogue: D[8*q + 4*(lane/32) + j][lane%32] of each 32x32 tile is acc[4*q + j]
     const float *bias = p.bias ? p.bias + (int64_t)tc.g * p.N : nullptr;
 #pragma unroll
@@ -292,170 +413,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
         }
 }
 
-// ---------------------------------------------------------------------------
-// 4-wave variant with direct-to-LDS loads (global_load_lds_dwordx4): each
-// wave instruction moves 64 x 16 bytes straight into a contiguous 1 KB LDS
-// region, so no staging registers are needed and the accumulators of a
-// 128 x 128 wave tile (256 registers) fit.  ST LDS stages (separate LDS
-// objects) keep ST-1 K tiles in flight; one barrier per K step.
-// ---------------------------------------------------------------------------
-__device__ inline void wait_vmcnt_le(int n) {
-    // s_waitcnt with only the vector-memory counter limited (gfx9 encoding)
-    switch (n) {
-#define MOE_VMW(N) case N: __builtin_amdgcn_s_waitcnt(((N) & 15) | (((N) >> 4) << 14) | (7 << 4) | (15 << 8)); break;
-        MOE_VMW(0) MOE_VMW(8) MOE_VMW(16) MOE_VMW(24) MOE_VMW(32) MOE_VMW(40) MOE_VMW(48)
-#undef MOE_VMW
-        default: __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); break;
-    }
-}
-
-template <int BK>
-__device__ inline int swz_k(int r) { return BK == 64 ? ((r >> 1) & 7) : ((r >> 2) & 3); }
-
-template <int BM, int BN, bool GLU, int BK, int ST>
-__global__ __launch_bounds__(256) void gemm_bf16_dma_kernel(GemmParams p) {
-    constexpr int NB = GLU ? 2 * BN : BN;
-    constexpr int WTM = BM / 2, WTN = BN / 2;
-    constexpr int TM = WTM / 32, TN = WTN / 32, TB = GLU ? 2 * TN : TN;
-    constexpr int CPR = BK / 8;        // 16-byte chunks per LDS row
-    constexpr int RPI = 64 / CPR;      // rows covered by one wave instruction
-    constexpr int AI = BM / RPI / 4;   // A instructions per wave per stage
-    constexpr int BI = NB / RPI / 4;   // B instructions per wave per stage
-    constexpr int STAGE = (BM + NB) * BK;
-    constexpr int KS = BK / 16;
-    static_assert(ST >= 2 && ST <= 4, "stages");
-    static_assert(AI >= 1 && BI >= 1 && (!GLU || BN % RPI == 0), "tile");
-    __shared__ __attribute__((aligned(1024))) bf16 L0[STAGE];
-    __shared__ __attribute__((aligned(1024))) bf16 L1[STAGE];
-    __shared__ __attribute__((aligned(1024))) bf16 L2[ST > 2 ? STAGE : 8];
-    __shared__ __attribute__((aligned(1024))) bf16 L3[ST > 3 ? STAGE : 8];
-    auto stage = [&](int s) -> bf16 * { return s == 0 ? L0 : s == 1 ? L1 : s == 2 ? L2 : L3; };
-
-    const int ntn = (p.N + BN - 1) / BN;
-    const TileCoord tc = find_tile<BM>(xcd_remap(blockIdx.x), p.offsets, p.mstart, p.G, p.rows, ntn);
-    if (!tc.valid) return;
-    const int n0 = tc.nt * BN;
-    const int64_t K = p.K;
-    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-    const int wm = wave % 2, wn = wave / 2;
-
-    const char *abase = (const char *)(p.A + tc.row0 * K);
-    const char *b0base = (const char *)(p.B0 + ((int64_t)tc.g * p.N + n0) * K);
-    const char *b1base = GLU ? (const char *)(p.B1 + ((int64_t)tc.g * p.N + n0) * K) : nullptr;
-    // per-lane byte offsets of this wave's DMA instructions (rows clamped)
-    uint32_t aoff[AI], boff[BI];
-#pragma unroll
-    for (int i = 0; i < AI; ++i) {
-        const int r = (wave * AI + i) * RPI + lane / CPR;
-        const int c = (lane % CPR) ^ swz_k<BK>(r);
-        int64_t rr = r;
-        if (tc.row0 + rr >= tc.row_end) rr = tc.row_end - 1 - tc.row0;
-        aoff[i] = (uint32_t)((rr * K + c * 8) * 2);
-    }
-#pragma unroll
-    for (int i = 0; i < BI; ++i) {
-        const int r = (wave * BI + i) * RPI + lane / CPR;  // row inside the B tile (gate rows, then up rows)
-        const int c = (lane % CPR) ^ swz_k<BK>(r);
-        int rn = (GLU && r >= BN) ? r - BN : r;
-        if (n0 + rn >= p.N) rn = p.N - 1 - n0;
-        boff[i] = (uint32_t)(((int64_t)rn * K + c * 8) * 2);
-    }
-    auto dma = [&](int kt, int s) {
-        bf16 *L = stage(s);
-        const int64_t ko = (int64_t)kt * BK * 2;
-#pragma unroll
-        for (int i = 0; i < AI; ++i)
-            __builtin_amdgcn_global_load_lds((const void *)(abase + ko + aoff[i]),
-                                             (__attribute__((address_space(3))) void *)(L + (wave * AI + i) * RPI * BK),
-                                             16, 0, 0);
-#pragma unroll
-        for (int i = 0; i < BI; ++i) {
-            const int r0 = (wave * BI + i) * RPI;
-            const char *bb = (GLU && r0 >= BN) ? b1base : b0base;
-            __builtin_amdgcn_global_load_lds((const void *)(bb + ko + boff[i]),
-                                             (__attribute__((address_space(3))) void *)(L + (BM + r0) * BK), 16, 0,
-                                             0);
-        }
-    };
-
-    f32x16 acc[TM][TB];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TB; ++j) acc[i][j] = f32x16{};
-    const int ra0 = wm * WTM + lane % 32;
-    const int rb0 = wn * WTN + lane % 32;
-    const int sa = swz_k<BK>(ra0), sb = swz_k<BK>(rb0);
-    bf16x8 fa[2][TM], fb[2][TB];
-    auto fload = [&](const bf16 *L, int ks, int slot) {
-        const int ch = ks * 2 + lane / 32;
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-            fa[slot][i] = __builtin_bit_cast(bf16x8, load16(L + (ra0 + i * 32) * BK + ((ch ^ sa) * 8)));
-#pragma unroll
-        for (int j = 0; j < TB; ++j)
-            fb[slot][j] = __builtin_bit_cast(
-                bf16x8, load16(L + (BM + (j >= TN ? BN : 0) + rb0 + (j % TN) * 32) * BK + ((ch ^ sb) * 8)));
-    };
-    auto compute = [&](const bf16 *L) {
-        fload(L, 0, 0);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            if (ks + 1 < KS) fload(L, ks + 1, (ks + 1) & 1);
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TB; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks & 1][i], fb[ks & 1][j], acc[i][j],
-                                                                        0, 0, 0);
-        }
-    };
-
-    const int KT = p.K / BK;
-#pragma unroll
-    for (int s = 0; s < ST - 1; ++s) dma(min(s, KT - 1), s);
-    // step k: wait for this wave's DMA of tile k, barrier (all DMAs of tile k
-    // landed, every wave done with stage (k-1) % ST), refill that stage with
-    // tile k+ST-1, compute tile k.  Unrolled by ST so stages are static.
-    for (int k0 = 0; k0 < KT; k0 += ST) {
-#pragma unroll
-        for (int u = 0; u < ST; ++u) {
-            const int k = k0 + u;
-            if (k < KT) {
-                wait_vmcnt_le((ST - 2) * (AI + BI));
-                __syncthreads();
-                dma(min(k + ST - 1, KT - 1), (u + ST - 1) % ST);
-                compute(stage(u));
-            }
-        }
-    }
-
-    const float *bias = p.bias ? p.bias + (int64_t)tc.g * p.N : nullptr;
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int col = n0 + wn * WTN + j * 32 + lane % 32;
-            if (col >= p.N) continue;
-            const float bcol = bias ? bias[col] : 0.f;
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int64_t row = tc.row0 + wm * WTM + i * 32 + 8 * q + 4 * (lane / 32) + jj;
-                    if (row >= tc.row_end) continue;
-                    float v = acc[i][j][4 * q + jj];
-                    if constexpr (GLU) v = silu(v) * acc[i][TN + j][4 * q + jj];
-                    else v = apply_act(p.act, v + bcol);
-                    p.C[row * p.N + col] = (bf16)v;
-                }
-        }
-}
-
-// ---------------------------------------------------------------------------
-// float32 grouped GEMM on the vector ALUs: 64x64 tiles, 4x4 outputs per
-// thread, K in steps of 16 through LDS.
-// ---------------------------------------------------------------------------
 struct GemmParamsF32 {
     const float *A;
     const float *B0;
@@ -541,8 +498,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParamsF32 p) {
 // tile plan
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void tile_plan_kernel(const int32_t *__restrict__ counts, int E, int BM,
-                                                       int32_t *__restrict__ mstart) {
+                                                       int32_t *__restrict__ mstart, int32_t *__restrict__ cnt,
+                                                       int ncnt) {
     const int lane = threadIdx.x;
+    for (int i = lane; i < ncnt; i += kWave) cnt[i] = 0;
     int base = 0;
     for (int e0 = 0; e0 < E; e0 += kWave) {
         const int e = e0 + lane;
@@ -559,8 +518,21 @@ __global__ __launch_bounds__(64) void tile_plan_kernel(const int32_t *__restrict
     if (lane == 0) mstart[E] = base;
 }
 
-void launch_tile_plan(const int32_t *counts, int E, int BM, int32_t *mstart, hipStream_t s) {
-    hipLaunchKernelGGL(tile_plan_kernel, dim3(1), dim3(64), 0, s, counts, E, BM, mstart);
+void launch_tile_plan(const int32_t *counts, int E, int BM, int32_t *mstart, int32_t *cnt, int ncnt,
+                      hipStream_t s) {
+    hipLaunchKernelGGL(tile_plan_kernel, dim3(1), dim3(64), 0, s, counts, E, BM, mstart, cnt, cnt ? ncnt : 0);
+}
+
+int device_cus() {
+    constexpr int kMaxDevices = 64;
+    static int cache[kMaxDevices] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+    if (dev < kMaxDevices && cache[dev] > 0) return cache[dev];
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (dev < kMaxDevices) cache[dev] = cus;
+    return cus;
 }
 
 // ---------------------------------------------------------------------------
@@ -585,12 +557,32 @@ static int64_t grid_for(const GemmArgs &a, int BM, int BN) {
 
 template <int BM, int BN, int WM, int WN, bool GLU, bool FB = true, int PD = 2, bool SB = false>
 static void launch_bf16_t(const GemmArgs &a, hipStream_t s) {
+    constexpr int NB = GLU ? 2 * BN : BN;
+    static_assert((int64_t)BM * NB <= kSplitUnitFloats, "split-K unit");
+    auto kern = gemm_bf16_kernel<BM, BN, WM, WN, GLU, FB, PD, SB>;
     GemmParams p{(const bf16 *)a.A, (const bf16 *)a.B0, (const bf16 *)a.B1, a.bias, (bf16 *)a.C,
-                 a.offsets, a.mstart, a.G, a.rows, a.N, a.K, a.act};
-    const int64_t grid = grid_for(a, BM, BN);
+                 a.offsets, a.mstart, a.G, a.rows, a.N, a.K, a.act, nullptr, nullptr, 0, 1};
+    int64_t grid = grid_for(a, BM, BN);
     if (grid == 0) return;
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, GLU, FB, PD, SB>), dim3((unsigned)grid), dim3(64 * WM * WN), 0, s,
-                       p);
+    // Split K of the last round needs the number of co-resident workgroups
+    // and room for that many partial tiles; otherwise it stays off.
+    const int KT = a.K / 64;
+    if (a.split.part != nullptr && KT >= 16) {
+        static int per_cu = -1;
+        if (per_cu < 0) {
+            int n = 0;
+            per_cu = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, 64 * WM * WN, 0) == hipSuccess ? n : 0;
+        }
+        const int64_t slots = (int64_t)device_cus() * per_cu;
+        if (slots > 0 && slots <= a.split.ncnt && slots * BM * NB <= a.split.part_floats) {
+            p.part = a.split.part;
+            p.cnt = a.split.cnt;
+            p.slots = (int)slots;
+            p.max_split = std::min(8, KT / 8);
+            grid += (slots + kGridQuantum - 1) / kGridQuantum * kGridQuantum;
+        }
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * WM * WN), 0, s, p);
 }
 
 template <bool GLU>

@@ -54,7 +54,22 @@ void launch_gather_rows(const void *x, const int32_t *row_token, const int32_t *
 
 // ---- expert FFN ----
 // Tile plan: mstart[e] = sum over experts e' < e of ceil(counts[e'] / BM), mstart[E] = total.
-void launch_tile_plan(const int32_t *counts, int E, int BM, int32_t *mstart, hipStream_t s);
+// mstart[e] = first m-tile of expert e (exclusive scan of ceil(counts/BM));
+// also clears the split-K arrival counters cnt[0 .. ncnt) (cnt may be null).
+void launch_tile_plan(const int32_t *counts, int E, int BM, int32_t *mstart, int32_t *cnt, int ncnt,
+                      hipStream_t s);
+
+// Split-K workspace of the bf16 grouped GEMM: float32 partial tiles of the
+// last, partial round of tiles plus one arrival counter per split tile.
+constexpr int64_t kSplitUnitFloats = 256 * 256;  // largest BM x (gate + up) N tile
+constexpr int kSplitSlotsPerCu = 4;              // counters per CU (several workgroups per CU)
+struct SplitKWs {
+    float *part;       // null: no split K
+    int64_t part_floats;
+    int32_t *cnt;
+    int ncnt;
+};
+int device_cus();  // compute units of the current device
 
 struct GemmArgs {
     const void *A;          // [rows][K] dtype (row r of group g at offsets[g] + i)
@@ -69,6 +84,7 @@ struct GemmArgs {
     int N, K;
     int act;                // ActKind; kActSwiglu uses B1
     bool bf16;
+    SplitKWs split;         // bf16 only; part null = off
 };
 enum GemmShape { kGemmPrefill = 0, kGemmSmallM = 1, kGemmDecode = 2 };
 int gemm_block_m(int shape, bool bf16);

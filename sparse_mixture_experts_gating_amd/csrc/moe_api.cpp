@@ -168,6 +168,9 @@ moe_status derive(const moe_config *c, Derived *o) {
     const int kq = o->bf16 ? 64 : 16;
     if (o->d % kq || o->F % kq || o->Fs % kq)
         return fail(MOE_ERR_UNSUPPORTED, "d_model, d_ff and d_ff_shared must be multiples of %d for this dtype", kq);
+    // the GEMM tiles address up to 256 rows from a tile base with 32-bit byte offsets
+    if (std::max(std::max(o->d, o->F), o->Fs) > (1 << 21))
+        return fail(MOE_ERR_UNSUPPORTED, "d_model, d_ff and d_ff_shared must be at most %d", 1 << 21);
     o->slots = o->ec ? o->E * o->capacity : o->T * o->k;
     o->a_max = o->slots;
     o->S = o->ec ? o->E : o->k;
@@ -218,13 +221,25 @@ LossWs carve_losses(const Derived &D, Carve &c) {
 }
 
 struct FfnWs {
-    size_t mstart, h, hs;
+    size_t mstart, h, hs, part, cnt;
+    int64_t part_floats;
+    int ncnt;
 };
 FfnWs carve_ffn(const Derived &D, Carve &c) {
     FfnWs w{};
     w.mstart = c.take((size_t)(D.E + 1) * 4);
     w.h = c.take((size_t)D.a_max * D.F * D.elem);
     w.hs = D.Fs ? c.take((size_t)D.T * D.Fs * D.elem) : 0;
+    if (D.bf16) {
+        // split-K partial tiles: one largest tile per CU (the bf16 shapes with
+        // several workgroups per CU have proportionally smaller tiles)
+        int cus = device_cus();
+        if (cus <= 0) cus = 256;
+        w.part_floats = (int64_t)cus * kSplitUnitFloats;
+        w.ncnt = cus * kSplitSlotsPerCu;
+        w.part = c.take((size_t)w.part_floats * 4);
+        w.cnt = c.take((size_t)w.ncnt * 4);
+    }
     return w;
 }
 
@@ -332,21 +347,23 @@ moe_status do_ffn(const Derived &D, const void *x_perm, const void *x, const moe
     const int BM = gemm_block_m(shape, D.bf16);
     int32_t *mstart = (int32_t *)(ws + fw.mstart);
     void *H = ws + fw.h;
-    TRY(launch(K_TILE_PLAN, s, [&] { launch_tile_plan(r->counts, (int)D.E, BM, mstart, s); }));
+    const SplitKWs split{D.bf16 ? (float *)(ws + fw.part) : nullptr, fw.part_floats,
+                         D.bf16 ? (int32_t *)(ws + fw.cnt) : nullptr, fw.ncnt};
+    TRY(launch(K_TILE_PLAN, s, [&] { launch_tile_plan(r->counts, (int)D.E, BM, mstart, split.cnt, split.ncnt, s); }));
     GemmArgs g1{x_perm, w->w1, w->w3, w->b1, H, r->offsets, mstart, (int)D.E, D.a_max, (int)D.F, (int)D.d,
-                D.act == MOE_ACT_SWIGLU ? kActSwiglu : D.act, D.bf16};
+                D.act == MOE_ACT_SWIGLU ? kActSwiglu : D.act, D.bf16, split};
     TRY(launch(K_GEMM1, s, [&] { launch_grouped_gemm(g1, shape, s); }));
     GemmArgs g2{H, w->w2, nullptr, w->b2, y_perm, r->offsets, mstart, (int)D.E, D.a_max, (int)D.d, (int)D.F,
-                kActNone, D.bf16};
+                kActNone, D.bf16, split};
     TRY(launch(K_GEMM2, s, [&] { launch_grouped_gemm(g2, shape, s); }));
     if (D.Fs) {
         const int sshape = D.T <= 32 ? kGemmDecode : kGemmPrefill;
         void *Hs = ws + fw.hs;
         GemmArgs s1{x, w->ws1, w->ws3, nullptr, Hs, nullptr, nullptr, 1, D.T, (int)D.Fs, (int)D.d, kActSwiglu,
-                    D.bf16};
+                    D.bf16, split};
         TRY(launch(K_GEMM1_SHARED, s, [&] { launch_grouped_gemm(s1, sshape, s); }));
         GemmArgs s2{Hs, w->ws2, nullptr, nullptr, y_shared, nullptr, nullptr, 1, D.T, (int)D.d, (int)D.Fs,
-                    kActNone, D.bf16};
+                    kActNone, D.bf16, split};
         TRY(launch(K_GEMM2_SHARED, s, [&] { launch_grouped_gemm(s2, sshape, s); }));
     }
     return MOE_OK;

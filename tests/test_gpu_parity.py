@@ -159,6 +159,16 @@ def test_expert_choice_permute_bit_exact():
 # ---------------------------------------------------------------------------
 
 FFN_SPECS = workloads.SMALL + [workloads.MIXTRAL_DECODE_BF16.replace(name="mixtral_decode_d512", d=512, F=1024)]
+# Few tiles and long K loops: the last (here: only) round of tiles is split
+# along K into 2..4 parts whose float32 partials are added by the last part.
+SPLITK_SPECS = [
+    workloads.MIXTRAL_PREFILL_BF16.replace(name="splitk_prefill_tiles", T=1000, d=2048, F=1024),
+    workloads.MIXTRAL_PREFILL_BF16.replace(name="splitk_small_m_tiles", T=300, d=2048, F=512),
+    workloads.MIXTRAL_PREFILL_BF16.replace(name="splitk_decode_tiles", T=16, d=2048, F=2048),
+    workloads.DEEPSEEK_SHARED_BF16.replace(name="splitk_shared_expert", T=520, d=1024, E=64, F=256,
+                                           F_shared=1024),
+]
+FFN_SPECS = FFN_SPECS + SPLITK_SPECS
 
 
 @pytest.mark.parametrize("spec", FFN_SPECS, ids=lambda s: s.name)
@@ -204,6 +214,16 @@ def test_expert_ffn_matches_oracle(spec):
     if spec.F_shared:
         ref = oracle.expert_ffn("swiglu", inp["x"], inp["ws1"], inp["ws3"], inp["ws2"])
         assert rel_err(_np(y_shared), ref) <= TOL[spec.dtype]
+
+
+@pytest.mark.parametrize("spec", SPLITK_SPECS[:1] + SPLITK_SPECS[3:], ids=lambda s: s.name)
+def test_split_k_forward_is_deterministic_and_matches_oracle(spec):
+    inp = workloads.make_inputs(spec)
+    dinp = to_dev(inp)
+    y1, routing = run_forward(spec, dinp)
+    y2, _ = run_forward(spec, dinp)
+    assert torch.equal(y1, y2)  # partials are added in part order, whatever the arrival order
+    _check_layer(spec, inp, y1, routing, oracle.forward(spec, inp))
 
 
 @pytest.mark.parametrize("spec", workloads.SMALL, ids=lambda s: s.name)
