@@ -54,6 +54,38 @@ def gemm1_bytes(spec, counts):
     return eb * (rows * spec.d + touched * nw * spec.F * spec.d + rows * spec.F)
 
 
+GEMM_SOURCES = ("gemm.hip", "common.h", "kernels.h")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "hbm_traffic_mixtral_prefill.md")
+
+
+def gemm_source_sha():
+    """Hash of the grouped-GEMM kernel sources (the counters in TRAFFIC_PROFILE
+    hold only for the kernel built from these exact files)."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in GEMM_SOURCES:
+        with open(os.path.join(ROOT, "sparse_mixture_experts_gating_amd", "csrc", name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed FETCH_SIZE / WRITE_SIZE
+    summary (rocprofv3, calibrated on a 1 GiB copy), or None when that summary is
+    for another workload or an older build of the GEMM kernel."""
+    if workload != "mixtral_8x7b_prefill_bf16" or not os.path.exists(TRAFFIC_PROFILE):
+        return None
+    with open(TRAFFIC_PROFILE) as f:
+        line = next((l for l in f if l.startswith("traffic-json: ")), None)
+    if line is None:
+        return None
+    rec = json.loads(line[len("traffic-json: "):])
+    if rec.get("gemm_source_sha") != gemm_source_sha() or kernel not in rec.get("kernels", {}):
+        return None
+    k = rec["kernels"][kernel]
+    return dict(bytes=k["fetch_bytes"] + k["write_bytes"], read=k["fetch_bytes"], written=k["write_bytes"])
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -137,9 +169,15 @@ def main():
         unit = "TFLOP/s"
     else:
         ach, bound, peak, unit = None, "hbm", PEAK_HBM_GBS, "GB/s"
+    traffic = measured_traffic(spec.name, dominant)
     roofline = dict(bound=bound, kernel=dominant, achieved=None if ach is None else round(ach, 2), peak=peak,
-                    unit=unit, frac=None if ach is None else round(ach / peak, 4), traffic=None,
+                    unit=unit, frac=None if ach is None else round(ach / peak, 4),
+                    traffic=None if traffic is None else traffic["bytes"],
                     avg_launch_us=kern[dominant]["avg_us"])
+    if traffic is not None:
+        alg = gemm1_bytes(spec, counts) if dominant == "gemm1_act" else None
+        roofline["traffic_detail"] = dict(unit="bytes per launch", read=traffic["read"], written=traffic["written"],
+                                          algorithmic=alg, source="profiles/hbm_traffic_mixtral_prefill.md")
 
     if args.copy_probe_mib:
         n = args.copy_probe_mib * (1 << 20)
