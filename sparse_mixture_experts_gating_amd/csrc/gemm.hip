@@ -566,8 +566,11 @@ static void launch_bf16_t(const GemmArgs &a, hipStream_t s) {
     if (grid == 0) return;
     // Split K of the last round needs the number of co-resident workgroups
     // and room for that many partial tiles; otherwise it stays off.
+    // Only for the 256-row tiles and long K loops: each split tile pays a
+    // release/acquire pair (an L2 write-back and invalidate on this XCD)
+    // that short tiles do not amortise (measured slower on decode shapes).
     const int KT = a.K / 64;
-    if (a.split.part != nullptr && KT >= 16) {
+    if (a.split.part != nullptr && BM == 256 && KT >= 64) {
         static int per_cu = -1;
         if (per_cu < 0) {
             int n = 0;
@@ -578,7 +581,7 @@ static void launch_bf16_t(const GemmArgs &a, hipStream_t s) {
             p.part = a.split.part;
             p.cnt = a.split.cnt;
             p.slots = (int)slots;
-            p.max_split = std::min(8, KT / 8);
+            p.max_split = std::min(8, KT / 32);
             grid += (slots + kGridQuantum - 1) / kGridQuantum * kGridQuantum;
         }
     }
