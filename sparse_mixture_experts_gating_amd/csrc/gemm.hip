@@ -162,13 +162,22 @@ __device__ inline int total_tiles(int BM, int ntn, const int32_t *offsets, const
 // of each step (scheduling barrier).  FB: double-buffer MFMA fragments.
 // IL: 0 = compiler schedule; 1 = the next substep's LDS reads interleaved
 // 1:1 with this substep's MFMAs; 2 = all next-substep reads first, then the MFMAs.
-template <int BM, int BN, int WM, int WN, bool GLU, bool FB, int PD = 2, bool SB = true, int IL = 0>
+// MF: MFMA tile edge, 32 (v_mfma_f32_32x32x16_bf16) or 16
+// (v_mfma_f32_16x16x32_bf16).  Both give the same flops per cycle, but with
+// switching operands the 16x16x32 form sustains about 15% more flops under
+// the socket power limit (2.06 vs 1.79 PFLOP/s in a register-only loop).
+template <int BM, int BN, int WM, int WN, bool GLU, bool FB, int PD = 2, bool SB = true, int IL = 0, int MF = 32>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
     constexpr int NT = 64 * WM * WN;  // threads
     constexpr int BK = 64;
     constexpr int NB = GLU ? 2 * BN : BN;
     constexpr int WTM = BM / WM, WTN = BN / WN;
-    constexpr int TM = WTM / 32, TN = WTN / 32;
+    static_assert(MF == 32 || MF == 16, "MFMA shape");
+    constexpr int KSUB = MF == 32 ? 16 : 32;   // k per MFMA
+    constexpr int NSUB = BK / KSUB;            // k-substeps per K tile
+    constexpr int AR = MF * MF / 64;           // accumulator registers per MFMA tile
+    using acc_t = float __attribute__((ext_vector_type(AR)));
+    constexpr int TM = WTM / MF, TN = WTN / MF;
     constexpr int TB = GLU ? 2 * TN : TN;  // B fragments per k-substep (gate then up)
     constexpr int RSTEP = NT / 8;          // rows between a thread's successive 16-byte chunks
     constexpr int A_PER_T = BM / RSTEP, B_PER_T = NB / RSTEP;
@@ -224,15 +233,18 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
     // all of a thread's rows (they differ by multiples of 16), so one base
     // address plus compile-time strides covers them.
     const int sdst = r0 * BK + ((ch0 ^ swz(r0)) * 8);
-    const int sw_a = swz(wm * WTM + lane % 32);
-    const int sw_b = swz(wn * WTN + lane % 32);
-    const int fa0 = (wm * WTM + lane % 32) * BK, fb0 = (BM + wn * WTN + lane % 32) * BK;
+    // MFMA operand lanes: lane l holds row (l % MF) of a fragment and the
+    // 16-byte k chunk l / MF of the k-substep; rows of one wave's fragments
+    // differ by multiples of 16, so they share one swizzle.
+    const int sw_a = swz(wm * WTM + lane % MF);
+    const int sw_b = swz(wn * WTN + lane % MF);
+    const int fa0 = (wm * WTM + lane % MF) * BK, fb0 = (BM + wn * WTN + lane % MF) * BK;
 
-    f32x16 acc[TM][TB];
+    acc_t acc[TM][TB];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TB; ++j) acc[i][j] = f32x16{};
+        for (int j = 0; j < TB; ++j) acc[i][j] = acc_t{};
 
     // Two register sets keep two K tiles in flight (prefetch distance 2); the
     // loads are issued unconditionally (the tail re-reads the last tile) so the
@@ -258,32 +270,36 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
     };
     bf16x8 fa[FS][TM], fb[FS][TB];
     auto fload = [&](const bf16 *L, int ks, int slot) {
-        const int ch = ks * 2 + lane / 32;
+        const int ch = ks * (KSUB / 8) + lane / MF;
         const bf16 *La = L + fa0 + ((ch ^ sw_a) * 8);
         const bf16 *Lb = L + fb0 + ((ch ^ sw_b) * 8);
 #pragma unroll
-        for (int i = 0; i < TM; ++i) fa[slot][i] = __builtin_bit_cast(bf16x8, load16(La + i * 32 * BK));
+        for (int i = 0; i < TM; ++i) fa[slot][i] = __builtin_bit_cast(bf16x8, load16(La + i * MF * BK));
 #pragma unroll
         for (int j = 0; j < TB; ++j)
             fb[slot][j] = __builtin_bit_cast(bf16x8,
-                                             load16(Lb + ((j >= TN ? BN : 0) + (j % TN) * 32) * BK));
+                                             load16(Lb + ((j >= TN ? BN : 0) + (j % TN) * MF) * BK));
     };
     auto mfmas = [&](int slot) {
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int j = 0; j < TB; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0);
+            for (int j = 0; j < TB; ++j) {
+                if constexpr (MF == 32)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0);
+                else
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0);
+            }
     };
     // MFMAs of one K tile whose k-substep-0 fragments are already in slot 0
     auto compute = [&](const bf16 *L) {
 #pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
+        for (int ks = 0; ks < NSUB; ++ks) {
             if constexpr (FB) {
-                if (ks + 1 < BK / 16) fload(L, ks + 1, (ks + 1) & 1);
+                if (ks + 1 < NSUB) fload(L, ks + 1, (ks + 1) & 1);
                 mfmas(ks & 1);
                 if constexpr (IL == 1) {
-                    if (ks + 1 < BK / 16) {
+                    if (ks + 1 < NSUB) {
 #pragma unroll
                         for (int g = 0; g < TM + TB; ++g) {
                             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
@@ -292,7 +308,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 } else if constexpr (IL == 2) {
-                    if (ks + 1 < BK / 16) __builtin_amdgcn_sched_group_barrier(0x100, TM + TB, 0);
+                    if (ks + 1 < NSUB) __builtin_amdgcn_sched_group_barrier(0x100, TM + TB, 0);
                     __builtin_amdgcn_sched_group_barrier(0x008, TM * TB, 0);
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -354,7 +370,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
         // Publish this part's accumulators; the last part to arrive adds the
         // S parts in part order (the sum does not depend on arrival order)
         // and runs the epilogue.  Layout: 16-byte chunk q4 of acc[i][j] of
-        // thread tid at ((i * TB + j) * 4 + q4) * NT + tid.
+        // thread tid at ((i * TB + j) * (AR / 4) + q4) * NT + tid.
         constexpr int PER_UNIT = BM * NB;
         float *mine = p.part + ((int64_t)wi.unit * wi.S + wi.part) * PER_UNIT;
 #pragma unroll
@@ -362,9 +378,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
 #pragma unroll
             for (int j = 0; j < TB; ++j)
 #pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
+                for (int q4 = 0; q4 < AR / 4; ++q4) {
                     f32x4 v = {acc[i][j][4 * q4], acc[i][j][4 * q4 + 1], acc[i][j][4 * q4 + 2], acc[i][j][4 * q4 + 3]};
-                    *(f32x4 *)(mine + (((i * TB + j) * 4 + q4) * NT + tid) * 4) = v;
+                    *(f32x4 *)(mine + (((i * TB + j) * (AR / 4) + q4) * NT + tid) * 4) = v;
                 }
         __threadfence();
         __syncthreads();
@@ -378,8 +394,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
 #pragma unroll
             for (int j = 0; j < TB; ++j)
 #pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const int64_t o = (((i * TB + j) * 4 + q4) * NT + tid) * 4;
+                for (int q4 = 0; q4 < AR / 4; ++q4) {
+                    const int64_t o = (((i * TB + j) * (AR / 4) + q4) * NT + tid) * 4;
                     f32x4 v = *(const f32x4 *)(parts + o);
                     for (int sp = 1; sp < wi.S; ++sp) v += *(const f32x4 *)(parts + (int64_t)sp * PER_UNIT + o);
                     acc[i][j][4 * q4] = v[0];
@@ -390,26 +406,26 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
         if (tid == 0) p.cnt[wi.unit] = 0;  // ready for the next launch
     }
 
-    // epilogue: D[8*q + 4*(lane/32) + j][lane%32] of each 32x32 tile is acc[4*q + j]
+    // epilogue: accumulator r of a tile holds D[row][lane % MF] with
+    // row = 8*(r/4) + 4*(lane/32) + r%4 (32x32) or 4*(lane/16) + r (16x16)
     const float *bias = p.bias ? p.bias + (int64_t)tc.g * p.N : nullptr;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-            const int col = n0 + wn * WTN + j * 32 + lane % 32;
+            const int col = n0 + wn * WTN + j * MF + lane % MF;
             if (col >= p.N) continue;
             const float bcol = bias ? bias[col] : 0.f;
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int64_t row = tc.row0 + wm * WTM + i * 32 + 8 * q + 4 * (lane / 32) + jj;
-                    if (row >= tc.row_end) continue;
-                    float v = acc[i][j][4 * q + jj];
-                    if constexpr (GLU) v = silu(v) * acc[i][TN + j][4 * q + jj];
-                    else v = apply_act(p.act, v + bcol);
-                    p.C[row * p.N + col] = (bf16)v;
-                }
+            for (int r = 0; r < AR; ++r) {
+                const int rt = MF == 32 ? 8 * (r / 4) + 4 * (lane / 32) + r % 4 : 4 * (lane / 16) + r;
+                const int64_t row = tc.row0 + wm * WTM + i * MF + rt;
+                if (row >= tc.row_end) continue;
+                float v = acc[i][j][r];
+                if constexpr (GLU) v = silu(v) * acc[i][TN + j][r];
+                else v = apply_act(p.act, v + bcol);
+                p.C[row * p.N + col] = (bf16)v;
+            }
         }
 }
 
@@ -555,11 +571,11 @@ static int64_t grid_for(const GemmArgs &a, int BM, int BN) {
     return g;
 }
 
-template <int BM, int BN, int WM, int WN, bool GLU, bool FB = true, int PD = 2, bool SB = false>
+template <int BM, int BN, int WM, int WN, bool GLU, bool FB = true, int PD = 2, bool SB = false, int MF = 16>
 static void launch_bf16_t(const GemmArgs &a, hipStream_t s) {
     constexpr int NB = GLU ? 2 * BN : BN;
     static_assert((int64_t)BM * NB <= kSplitUnitFloats, "split-K unit");
-    auto kern = gemm_bf16_kernel<BM, BN, WM, WN, GLU, FB, PD, SB>;
+    auto kern = gemm_bf16_kernel<BM, BN, WM, WN, GLU, FB, PD, SB, 0, MF>;
     GemmParams p{(const bf16 *)a.A, (const bf16 *)a.B0, (const bf16 *)a.B1, a.bias, (bf16 *)a.C,
                  a.offsets, a.mstart, a.G, a.rows, a.N, a.K, a.act, nullptr, nullptr, 0, 1};
     int64_t grid = grid_for(a, BM, BN);
@@ -606,16 +622,18 @@ void launch_grouped_gemm(const GemmArgs &a, int shape, hipStream_t s) {
     }
     // Tile shapes measured on the Mixtral-shape prefill GEMMs (T=4096, k=2,
     // d=4096, F=14336): 8 waves (2 per SIMD) with 256-row tiles, two K tiles
-    // in flight, fragments double-buffered, loads left to the scheduler.
+    // in flight, fragments double-buffered, loads left to the scheduler, on
+    // 16x16x32 MFMAs (8-9% faster than 32x32x16 under the power limit).  The
+    // 128- and 32-row tiles stay on 32x32x16, which measured faster there.
     if (shape == kGemmDecode) {
-        if (glu) launch_bf16_t<32, 128, 1, 4, true>(a, s);
-        else launch_bf16_t<32, 128, 1, 4, false>(a, s);
+        if (glu) launch_bf16_t<32, 128, 1, 4, true, true, 2, false, 32>(a, s);
+        else launch_bf16_t<32, 128, 1, 4, false, true, 2, false, 32>(a, s);
     } else if (shape == kGemmSmallM) {
-        if (glu) launch_bf16_t<128, 128, 2, 2, true, true, 2, true>(a, s);
-        else launch_bf16_t<128, 256, 2, 2, false, true, 2, true>(a, s);
+        if (glu) launch_bf16_t<128, 128, 2, 2, true, true, 2, true, 32>(a, s);
+        else launch_bf16_t<128, 256, 2, 2, false, true, 2, true, 32>(a, s);
     } else {
-        if (glu) launch_bf16_t<256, 128, 2, 4, true, true, 2, false>(a, s);
-        else launch_bf16_t<256, 256, 2, 4, false, true, 2, false>(a, s);
+        if (glu) launch_bf16_t<256, 128, 2, 4, true, true, 2, false, 16>(a, s);
+        else launch_bf16_t<256, 256, 2, 4, false, true, 2, false, 16>(a, s);
     }
 }
 
