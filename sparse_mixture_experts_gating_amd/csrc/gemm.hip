@@ -158,6 +158,18 @@ __device__ inline int total_tiles(int BM, int ntn, const int32_t *offsets, const
     return mstart[G] * ntn;
 }
 
+// Calls f(std::integral_constant<int, NA>) with NA the smallest of 0, 1, 2, 4,
+// ..., TM that is at least n (TM a power of two).
+template <int NA, int TM, typename F>
+__device__ inline void dispatch_active(int n, F &&f) {
+    if constexpr (NA >= TM) {
+        f(std::integral_constant<int, TM>{});
+    } else {
+        if (n <= NA) f(std::integral_constant<int, NA>{});
+        else dispatch_active<NA == 0 ? 1 : 2 * NA, TM>(n, f);
+    }
+}
+
 // PD: K tiles in flight in registers (1: one set, loads issued a step ahead;
 // 2: two sets, loads issued two steps ahead).  SB: pin the loads at the head
 // of each step (scheduling barrier).  FB: double-buffer MFMA fragments.
@@ -165,10 +177,14 @@ __device__ inline int total_tiles(int BM, int ntn, const int32_t *offsets, const
 // 1:1 with this substep's MFMAs; 2 = all next-substep reads first, then the MFMAs.
 // MF: MFMA tile edge, 32 (v_mfma_f32_32x32x16_bf16) or 16
 // (v_mfma_f32_16x16x32_bf16).  Both give the same flops per cycle, but with
-// switching operands the 16x16x32 form sustains about 15% more flops under
-// the socket power limit (2.06 vs 1.79 PFLOP/s in a register-only loop).
+// switching operands the 16x16x32 form sustains more flops under the socket
+// power limit (2.06 vs 1.79 PFLOP/s in a register-only loop; 2.5% on the
+// whole grouped GEMM).
+// RMAP: waves w and w + 4, which share a SIMD, take different row halves (wm)
+// instead of the same one.  GSKIP: in a ragged last tile, run only the MFMAs
+// of the row blocks that hold rows of the expert.
 template <int BM, int BN, int WM, int WN, bool GLU, bool FB, int PD = 2, bool SB = true, int IL = 0, int MF = 32,
-          bool SKIP = false>
+          bool RMAP = false, bool GSKIP = true>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
     constexpr int NT = 64 * WM * WN;  // threads
     constexpr int BK = 64;
@@ -205,11 +221,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
 
     const int tid = threadIdx.x;
     const int wave = tid / kWave, lane = tid % kWave;
-    // SKIP: waves w and w + 4 share a SIMD; giving them different row halves
-    // (wm) lets a wave whose rows all lie past the expert's end skip its
-    // MFMAs and halve its SIMD's work in a ragged last tile.
-    const int wm = SKIP ? wave / WN : wave % WM, wn = SKIP ? wave % WN : wave / WM;
-    const bool wave_rows = !SKIP || tc.row0 + (int64_t)wm * WTM < tc.row_end;
+    const int wm = RMAP ? wave / WN : wave % WM, wn = RMAP ? wave % WN : wave / WM;
+    // MF-row blocks of this wave that hold rows of the expert: in a ragged
+    // last tile a wave runs the MFMAs (and A-fragment reads) of only the
+    // first NA blocks, NA = that count rounded up to a power of two; blocks
+    // past it lie wholly past the expert's last row.
+    const int64_t wrows = tc.row_end - (tc.row0 + (int64_t)wm * WTM);
+    const int nact = wrows <= 0 ? 0 : (wrows >= WTM ? TM : (int)((wrows + MF - 1) / MF));
 
     // Loads: buffer loads from uniform tile bases with 32-bit per-chunk byte
     // offsets; the K offset goes in the scalar offset.  The byte limit of
@@ -275,20 +293,22 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
         for (int i = 0; i < B_PER_T; ++i) store16(L + BM * BK + sdst + i * RSTEP * BK, rb[set][i]);
     };
     bf16x8 fa[FS][TM], fb[FS][TB];
-    auto fload = [&](const bf16 *L, int ks, int slot) {
+    auto fload = [&](const bf16 *L, int ks, int slot, auto na) {
+        constexpr int NA = decltype(na)::value;
         const int ch = ks * (KSUB / 8) + lane / MF;
         const bf16 *La = L + fa0 + ((ch ^ sw_a) * 8);
         const bf16 *Lb = L + fb0 + ((ch ^ sw_b) * 8);
 #pragma unroll
-        for (int i = 0; i < TM; ++i) fa[slot][i] = __builtin_bit_cast(bf16x8, load16(La + i * MF * BK));
+        for (int i = 0; i < NA; ++i) fa[slot][i] = __builtin_bit_cast(bf16x8, load16(La + i * MF * BK));
 #pragma unroll
         for (int j = 0; j < TB; ++j)
             fb[slot][j] = __builtin_bit_cast(bf16x8,
                                              load16(Lb + ((j >= TN ? BN : 0) + (j % TN) * MF) * BK));
     };
-    auto mfmas = [&](int slot) {
+    auto mfmas = [&](int slot, auto na) {
+        constexpr int NA = decltype(na)::value;
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < NA; ++i)
 #pragma unroll
             for (int j = 0; j < TB; ++j) {
                 if constexpr (MF == 32)
@@ -298,38 +318,39 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
             }
     };
     // MFMAs of one K tile whose k-substep-0 fragments are already in slot 0
-    auto compute = [&](const bf16 *L) {
+    auto compute = [&](const bf16 *L, auto na) {
+        constexpr int NA = decltype(na)::value;
 #pragma unroll
         for (int ks = 0; ks < NSUB; ++ks) {
             if constexpr (FB) {
-                if (ks + 1 < NSUB) fload(L, ks + 1, (ks + 1) & 1);
-                mfmas(ks & 1);
+                if (ks + 1 < NSUB) fload(L, ks + 1, (ks + 1) & 1, na);
+                mfmas(ks & 1, na);
                 if constexpr (IL == 1) {
                     if (ks + 1 < NSUB) {
 #pragma unroll
-                        for (int g = 0; g < TM + TB; ++g) {
+                        for (int g = 0; g < NA + TB; ++g) {
                             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                         }
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 } else if constexpr (IL == 2) {
-                    if (ks + 1 < NSUB) __builtin_amdgcn_sched_group_barrier(0x100, TM + TB, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x008, TM * TB, 0);
+                    if (ks + 1 < NSUB) __builtin_amdgcn_sched_group_barrier(0x100, NA + TB, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, NA * TB, 0);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             } else {
-                if (ks > 0) fload(L, ks, 0);
-                mfmas(0);
+                if (ks > 0) fload(L, ks, 0, na);
+                mfmas(0, na);
             }
         }
     };
 
-    // The K loop, with or without the MFMA work of this wave (the loads, LDS
-    // stores and barriers are the same in both, so every wave meets every
-    // barrier).
-    auto kloop = [&](auto mma) {
-        constexpr bool MMA = decltype(mma)::value;
+    // The K loop with the MFMA work of the first NA row blocks of this wave
+    // (the loads, LDS stores and barriers are the same for every NA, so every
+    // wave meets every barrier).
+    auto kloop = [&](auto na) {
+        constexpr bool MMA = decltype(na)::value > 0;
         if constexpr (PD == 1) {
             // one register set: tile kt+1 is loaded during step kt and stored into
             // the other LDS buffer at its end (the tail re-reads tile KT-1)
@@ -341,8 +362,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
                 gload(min(kt + 1, KT - 1), 0);
                 if constexpr (SB) __builtin_amdgcn_sched_barrier(0);
                 if constexpr (MMA) {
-                    fload(lds[cur], 0, 0);
-                    compute(lds[cur]);
+                    fload(lds[cur], 0, 0, na);
+                    compute(lds[cur], na);
                 }
                 lstore(cur ^ 1, 0);
                 __syncthreads();
@@ -361,32 +382,28 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
                 // even step: LDS buffer 0 holds tile kt, register set 1 holds tile kt+1
                 gload(min(kt + 2, KT - 1), 0);
                 if constexpr (SB) __builtin_amdgcn_sched_barrier(0);
-                if constexpr (MMA) fload(lds[0], 0, 0);
+                if constexpr (MMA) fload(lds[0], 0, 0, na);
                 lstore(1, 1);
-                if constexpr (MMA) compute(lds[0]);
+                if constexpr (MMA) compute(lds[0], na);
                 __syncthreads();
                 // odd step: LDS buffer 1 holds tile kt+1, register set 0 holds tile kt+2 (or KT-1)
                 gload(min(kt + 3, KT - 1), 1);
                 if constexpr (SB) __builtin_amdgcn_sched_barrier(0);
-                if constexpr (MMA) fload(lds[1], 0, 0);
+                if constexpr (MMA) fload(lds[1], 0, 0, na);
                 lstore(0, 0);
-                if constexpr (MMA) compute(lds[1]);
+                if constexpr (MMA) compute(lds[1], na);
                 __syncthreads();
             }
             if (kt < KT) {  // odd tile count: the last tile is in LDS buffer 0
                 if constexpr (MMA) {
-                    fload(lds[0], 0, 0);
-                    compute(lds[0]);
+                    fload(lds[0], 0, 0, na);
+                    compute(lds[0], na);
                 }
             }
         }
     };
-    if constexpr (SKIP) {
-        if (wave_rows) kloop(std::true_type{});
-        else kloop(std::false_type{});
-    } else {
-        kloop(std::true_type{});
-    }
+    if constexpr (GSKIP) dispatch_active<0, TM>(nact, kloop);
+    else kloop(std::integral_constant<int, TM>{});
 
     if (wi.S > 1) {
         // Publish this part's accumulators; the last part to arrive adds the
@@ -594,11 +611,11 @@ static int64_t grid_for(const GemmArgs &a, int BM, int BN) {
 }
 
 template <int BM, int BN, int WM, int WN, bool GLU, bool FB = true, int PD = 2, bool SB = false, int MF = 16,
-          bool SKIP = false>
+          bool RMAP = false, bool GSKIP = true, int IL = 0>
 static void launch_bf16_t(const GemmArgs &a, hipStream_t s) {
     constexpr int NB = GLU ? 2 * BN : BN;
     static_assert((int64_t)BM * NB <= kSplitUnitFloats, "split-K unit");
-    auto kern = gemm_bf16_kernel<BM, BN, WM, WN, GLU, FB, PD, SB, 0, MF, SKIP>;
+    auto kern = gemm_bf16_kernel<BM, BN, WM, WN, GLU, FB, PD, SB, IL, MF, RMAP, GSKIP>;
     GemmParams p{(const bf16 *)a.A, (const bf16 *)a.B0, (const bf16 *)a.B1, a.bias, (bf16 *)a.C,
                  a.offsets, a.mstart, a.G, a.rows, a.N, a.K, a.act, nullptr, nullptr, 0, 1};
     int64_t grid = grid_for(a, BM, BN);
@@ -645,11 +662,15 @@ void launch_grouped_gemm(const GemmArgs &a, int shape, hipStream_t s) {
     }
     // Tile shapes measured on the Mixtral-shape prefill GEMMs (T=4096, k=2,
     // d=4096, F=14336): 8 waves (2 per SIMD) with 256-row tiles, two K tiles
-    // in flight, fragments double-buffered, loads left to the scheduler, on
-    // 16x16x32 MFMAs (8-9% faster than 32x32x16 under the power limit).  The
-    // 128- and 32-row tiles stay on 32x32x16, which measured faster there.
-    // Skipping the MFMAs of waves past the expert's last row measured 4.7%
-    // faster on the down projection and 2% slower on the gate/up one.
+    // in flight, fragments double-buffered, on 16x16x32 MFMAs.  The 128- and
+    // 32-row tiles stay on 32x32x16, which measured faster there.
+    // Alternating single launches of two variants (so both see the same
+    // power and clock state) measured: 16x16x32 MFMAs 2.5% faster than
+    // 32x32x16 on both GEMMs; row halves split across the two waves of a
+    // SIMD (RMAP) 3% faster on the down projection and 1% slower on the
+    // gate/up one; LDS reads interleaved 1:1 with the MFMAs (IL = 1) 2.5%
+    // faster on the down projection, no change on the gate/up one; the
+    // row-block skip of ragged tiles (GSKIP) 0.8% faster on the gate/up one.
     if (shape == kGemmDecode) {
         if (glu) launch_bf16_t<32, 128, 1, 4, true, true, 2, false, 32>(a, s);
         else launch_bf16_t<32, 128, 1, 4, false, true, 2, false, 32>(a, s);
@@ -657,8 +678,8 @@ void launch_grouped_gemm(const GemmArgs &a, int shape, hipStream_t s) {
         if (glu) launch_bf16_t<128, 128, 2, 2, true, true, 2, true, 32>(a, s);
         else launch_bf16_t<128, 256, 2, 2, false, true, 2, true, 32>(a, s);
     } else {
-        if (glu) launch_bf16_t<256, 128, 2, 4, true, true, 2, false, 16>(a, s);
-        else launch_bf16_t<256, 256, 2, 4, false, true, 2, false, 16, true>(a, s);
+        if (glu) launch_bf16_t<256, 128, 2, 4, true, true, 2, false, 16, false, true, 0>(a, s);
+        else launch_bf16_t<256, 256, 2, 4, false, true, 2, false, 16, true, true, 1>(a, s);
     }
 }
 
