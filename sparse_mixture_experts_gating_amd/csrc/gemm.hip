@@ -85,21 +85,6 @@ __device__ inline TileCoord find_tile(int tile, const int32_t *offsets, const in
     return c;
 }
 
-// Raw buffer resource over `bytes` bytes from `base` (limit clamped to 2^31 - 1;
-// callers address at most a 256-row tile from the base).  Loads at offsets
-// at or past the limit return zeros.
-__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, int64_t bytes) {
-    const int64_t lim = bytes < 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : bytes);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)lim, 0x00020000);
-}
-__device__ inline u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) {
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, soff, 0));
-}
-
-// LDS tiles hold rows of 64 bf16 (128 bytes = eight 16-byte chunks).  Chunk c
-// of row r is stored at chunk slot c ^ swz(r) so that the 16-byte reads of 16
-// consecutive rows at one chunk index touch distinct banks.
-__device__ inline int swz(int r) { return (r >> 1) & 7; }
 
 struct GemmParams {
     const bf16 *A;

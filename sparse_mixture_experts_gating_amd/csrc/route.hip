@@ -78,9 +78,9 @@ __device__ void gate_one_token(const float *row, int E, int k, int gating, int64
     }
 }
 
-// Router GEMM on bf16 MFMA (v_mfma_f32_16x16x32_bf16) + gating epilogue.
-// A block owns 16*WM tokens; its 4 waves form WM (tokens) x WK (K split)
-// with WM*WK = 4.  Each wave computes 16 tokens x 16*NT experts over its K
+// Router GEMM on bf16 MFMA (v_mfma_f32_16x16x32_bf16) + gating epilogue, for
+// up to 64 experts.  A block owns 16*WM tokens; its 4 waves form WM (tokens)
+// x WK (K split) with WM*WK = 4.  Each wave computes 16 tokens x 16*NT experts over its K
 // range, straight from global memory (x rows are read once; the router
 // weights stay in L1/L2).  Partial sums meet in LDS in a fixed order, the
 // bias is added, logits are written, and each wave gates whole tokens.
@@ -463,8 +463,159 @@ __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(const float *__re
 }
 
 // ---------------------------------------------------------------------------
+// Router GEMM with LDS-staged operand tiles and the gating epilogue.
+// A block owns TOK tokens and all E experts (padded to EP; with the noisy
+// router, EP more columns hold the noise projection x.Wn).  Each K chunk of
+// 64 moves the x rows and the weight rows through registers into one of two
+// XOR-swizzled LDS buffers (rows past T or E read as zeros through the
+// buffer-load limit), and the 4 waves split the columns: wave w computes
+// TOK tokens x EPX/4 columns on v_mfma_f32_16x16x32_bf16.  The float32
+// logits then meet in LDS, the bias (and softplus(x.Wn) * noise) is added in
+// a fixed order, and each wave gates whole tokens.
+// ---------------------------------------------------------------------------
+template <int TOK, int EP, bool NOISY, int PD = 4>
+__global__ __launch_bounds__(256) void router_tile_kernel(
+    const bf16 *__restrict__ x, const bf16 *__restrict__ wg, const float *__restrict__ bias, int T, int d, int E,
+    int k, int gating, float *__restrict__ logits, int32_t *__restrict__ idx_out, float *__restrict__ w_out,
+    const bf16 *__restrict__ wn, const float *__restrict__ noise) {
+    constexpr int BK = 64;
+    constexpr int EPX = NOISY ? 2 * EP : EP;  // B rows: router weights, then the noise projection
+    constexpr int ROWS = TOK + EPX;           // LDS rows per buffer
+    constexpr int WTN = EPX / 4;              // columns per wave
+    constexpr int TM = TOK / 16, TN = WTN / 16;
+    constexpr int XPT = TOK / 32, WPT = EPX / 32;  // 16-byte chunks per thread and K chunk
+    static_assert(TM >= 1 && TN >= 1 && XPT >= 1 && WPT >= 1, "router tile");
+    static_assert(2 * ROWS * BK * 2 >= TOK * EPX * 4, "the logits tile reuses the staging buffers");
+    __shared__ __attribute__((aligned(16))) bf16 lds[2][ROWS * BK];
+
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    const int64_t tok0 = (int64_t)blockIdx.x * TOK;
+    const int r0 = tid / 8, ch0 = tid % 8;  // thread moves chunk ch0 of rows r0 + 32*i
+    const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(x + tok0 * d, (T - tok0) * (int64_t)d * 2);
+    const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(wg, (int64_t)E * d * 2);
+    const __amdgpu_buffer_rsrc_t nr = NOISY ? buffer_rsrc(wn, (int64_t)E * d * 2) : wr;
+    uint32_t xoff[XPT], woff[WPT];
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) xoff[i] = (uint32_t)(((int64_t)(r0 + 32 * i) * d + ch0 * 8) * 2);
+#pragma unroll
+    for (int i = 0; i < WPT; ++i) {
+        const int r = r0 + 32 * i;
+        woff[i] = (uint32_t)(((int64_t)(NOISY && r >= EP ? r - EP : r) * d + ch0 * 8) * 2);
+    }
+    // rows r0 + 32*i (and TOK + r0 + 32*i, TOK a multiple of 16) share swz(r0)
+    const int sdst = r0 * BK + ((ch0 ^ swz(r0)) * 8);
+    // PD register sets: chunk c is loaded into set c % PD, PD chunks ahead of
+    // its MFMAs, so PD - 1 chunks stay in flight while one is computed.
+    u32x4 rx[PD][XPT], rw[PD][WPT];
+    auto gload = [&](int kc, int set) {
+        const int ko = kc * BK * 2;
+#pragma unroll
+        for (int i = 0; i < XPT; ++i) rx[set][i] = buffer_load16(xr, xoff[i], ko);
+#pragma unroll
+        for (int i = 0; i < WPT; ++i) rw[set][i] = buffer_load16(NOISY && 32 * i >= EP ? nr : wr, woff[i], ko);
+    };
+    auto lstore = [&](bf16 *L, int set) {
+#pragma unroll
+        for (int i = 0; i < XPT; ++i) store16(L + sdst + i * 32 * BK, rx[set][i]);
+#pragma unroll
+        for (int i = 0; i < WPT; ++i) store16(L + TOK * BK + sdst + i * 32 * BK, rw[set][i]);
+    };
+    f32x4 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // fragment lanes: row lane % 16, 16-byte k chunk lane / 16 of a 32-k substep
+    const int sw = swz(lane % 16);
+    const int fa0 = (lane % 16) * BK, fb0 = (TOK + wave * WTN + lane % 16) * BK;
+    auto compute = [&](const bf16 *L) {
+#pragma unroll
+        for (int ks = 0; ks < BK / 32; ++ks) {
+            const int c = ((ks * 4 + lane / 16) ^ sw) * 8;
+            bf16x8 fa[TM], fb[TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i) fa[i] = __builtin_bit_cast(bf16x8, load16(L + fa0 + i * 16 * BK + c));
+#pragma unroll
+            for (int j = 0; j < TN; ++j) fb[j] = __builtin_bit_cast(bf16x8, load16(L + fb0 + j * 16 * BK + c));
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        }
+    };
+    const int nk = d / BK;
+#pragma unroll
+    for (int c = 0; c < PD; ++c) gload(min(c, nk - 1), c);
+    lstore(lds[0], 0);
+    __syncthreads();
+    // chunk kc: refill its set's predecessor (set kc % PD, stored at the end
+    // of the previous chunk) with chunk kc + PD, compute chunk kc from LDS,
+    // store chunk kc + 1 into the other LDS buffer.  Past the last chunk the
+    // loads re-read chunk nk - 1 and the stores fill a buffer nobody reads.
+    for (int k0 = 0; k0 < nk; k0 += PD) {
+#pragma unroll
+        for (int u = 0; u < PD; ++u) {
+            const int kc = k0 + u;
+            if (kc < nk) {
+                gload(min(kc + PD, nk - 1), u);
+                compute(lds[kc & 1]);
+                lstore(lds[(kc + 1) & 1], (u + 1) % PD);
+                __syncthreads();
+            }
+        }
+    }
+    // float32 logits tile [TOK][EPX] in the (now free) staging buffers;
+    // D[4*(lane/16) + q][lane % 16] of each 16x16 tile is acc[q]
+    float *Lf = reinterpret_cast<float *>(&lds[0][0]);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                Lf[(i * 16 + 4 * (lane / 16) + q) * EPX + wave * WTN + j * 16 + lane % 16] = acc[i][j][q];
+    __syncthreads();
+    for (int tt = wave; tt < TOK; tt += 4) {
+        const int64_t t = tok0 + tt;
+        if (t >= T) break;
+        float *row = Lf + tt * EPX;
+        // lane l owns experts l + 64q, the entries gate_one_token reads back
+        for (int e = lane; e < E; e += kWave) {
+            float v = row[e];
+            if (bias) v += bias[e];
+            if constexpr (NOISY) v += softplus(row[EP + e]) * noise[t * E + e];
+            row[e] = v;
+            if (logits) logits[t * E + e] = v;
+        }
+        if (gating != kGateExpertChoice) gate_one_token(row, E, k, gating, t, idx_out, w_out);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
+template <int TOK, int EP>
+static void launch_router_tile_t(const RouteArgs &a, hipStream_t s) {
+    const int grid = (a.T + TOK - 1) / TOK;
+    // register sets in flight: four, or two when a set is large (noisy, 256 experts)
+    constexpr int PDN = (TOK + 2 * EP) / 32 <= 10 ? 4 : 2;
+    if (a.wn)
+        hipLaunchKernelGGL((router_tile_kernel<TOK, EP, true, PDN>), dim3(grid), dim3(256), 0, s, (const bf16 *)a.x,
+                           (const bf16 *)a.wg, a.bias, a.T, a.d, a.E, a.k, a.gating, a.logits, a.idx, a.w,
+                           (const bf16 *)a.wn, a.noise);
+    else
+        hipLaunchKernelGGL((router_tile_kernel<TOK, EP, false>), dim3(grid), dim3(256), 0, s, (const bf16 *)a.x,
+                           (const bf16 *)a.wg, a.bias, a.T, a.d, a.E, a.k, a.gating, a.logits, a.idx, a.w,
+                           nullptr, nullptr);
+}
+
+template <int TOK>
+static void launch_router_tile(const RouteArgs &a, hipStream_t s) {
+    if (a.E <= 128) launch_router_tile_t<TOK, 128>(a, s);
+    else launch_router_tile_t<TOK, 256>(a, s);
+}
+
 template <int WM, int NT>
 static void launch_route_bf16_t(const RouteArgs &a, hipStream_t s) {
     const int tok = 16 * WM;
@@ -487,11 +638,18 @@ void launch_route(const RouteArgs &a, hipStream_t s) {
                            (const float *)a.wn, a.noise);
         return;
     }
-    if (a.E <= 16) launch_route_bf16_t<1, 1>(a, s);
-    else if (a.E <= 32) launch_route_bf16_t<1, 2>(a, s);
-    else if (a.E <= 64) launch_route_bf16_t<1, 4>(a, s);
-    else if (a.E <= 128) launch_route_bf16_t<4, 8>(a, s);
-    else launch_route_bf16_t<4, 16>(a, s);
+    // More than 64 experts: LDS-staged tiles (the weight rows are shared by
+    // a block's tokens); up to 64, per-wave K slices straight from global
+    // memory, which measured faster for few experts.
+    if (a.E <= 64) {
+        if (a.E <= 16) launch_route_bf16_t<1, 1>(a, s);
+        else if (a.E <= 32) launch_route_bf16_t<1, 2>(a, s);
+        else launch_route_bf16_t<1, 4>(a, s);
+        return;
+    }
+    // 32-token blocks unless that already gives a block per CU twice over
+    if (a.T >= 64 * 512) launch_router_tile<64>(a, s);
+    else launch_router_tile<32>(a, s);
 }
 
 void launch_gate_logits(const float *logits, int T, int E, int k, int gating, int32_t *idx, float *w,
