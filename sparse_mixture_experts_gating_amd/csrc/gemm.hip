@@ -9,7 +9,7 @@
 // youngju.dev "Mixture of Experts（MoE）架构深度解析" SwiGLUExpert; [yj-ja]
 // youngju.dev "Sparse Mixture of Experts（MoE）アーキテクチャ深層分析" SwiGLUExpert).
 //
-// Tiles: a device-side plan (mstart) lists the m-tiles of every expert; the
+// Tiles: a device-side plan (mstart, m-tile table) lists the m-tiles of every expert; the
 // grid covers the worst case and surplus blocks exit.  Inside an expert with
 // Me m-tiles, tiles run in groups of Me x gN (m fastest, gN ~ 32 / Me weight
 // panels), and every XCD receives runs of 32 consecutive tiles: a run shares
@@ -49,9 +49,12 @@ __device__ inline void group_tile(int local, int mt, int ntn, int *m, int *n) {
     *n = grp * gn + within / mt;
 }
 
+// The m-tile table holds, for every m-tile of the plan, its expert's first
+// m-tile (x), the expert index (y) and the expert's rows [z, w).  Tile t of the grid belongs to m-tile t / ntn,
+// so one table load (next to the total) places it; no search over experts.
 template <int BM>
-__device__ inline TileCoord find_tile(int tile, const int32_t *offsets, const int32_t *mstart, int G,
-                                      int64_t rows, int ntn) {
+__device__ inline TileCoord find_tile(int tile, const int32_t *offsets, const int32_t *mstart, const int4 *mtile,
+                                      int max_mt, int G, int64_t rows, int ntn) {
     TileCoord c;
     c.valid = false;
     int m, n;
@@ -66,21 +69,16 @@ __device__ inline TileCoord find_tile(int tile, const int32_t *offsets, const in
         c.valid = true;
         return c;
     }
+    const int mt = tile / ntn;
+    const int4 info = mtile[mt < max_mt ? mt : max_mt - 1];
     const int total = mstart[G];
     if (tile >= total * ntn) return c;
-    int lo = 0, hi = G - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (mstart[mid] * ntn <= tile) lo = mid;
-        else hi = mid - 1;
-    }
-    const int local = tile - mstart[lo] * ntn;
-    const int mt_g = mstart[lo + 1] - mstart[lo];
-    group_tile(local, mt_g, ntn, &m, &n);
-    c.g = lo;
+    const int local = tile - info.x * ntn;
+    group_tile(local, (int)((info.w - info.z + BM - 1) / BM), ntn, &m, &n);
+    c.g = info.y;
     c.nt = n;
-    c.row0 = offsets[lo] + (int64_t)m * BM;
-    c.row_end = offsets[lo + 1];
+    c.row0 = info.z + (int64_t)m * BM;
+    c.row_end = info.w;
     c.valid = true;
     return c;
 }
@@ -94,6 +92,8 @@ struct GemmParams {
     bf16 *C;
     const int32_t *offsets;
     const int32_t *mstart;
+    const int4 *mtile;  // m-tile table of the plan (offsets non-null)
+    int max_mt;         // its capacity
     int G;
     int64_t rows;
     int N, K;
@@ -195,7 +195,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
     const WorkItem wi = work_item(xcd_remap(blockIdx.x),
                                   total_tiles(BM, ntn, p.offsets, p.mstart, p.G, p.rows), p);
     if (!wi.valid) return;
-    const TileCoord tc = find_tile<BM>(wi.tile, p.offsets, p.mstart, p.G, p.rows, ntn);
+    const TileCoord tc = find_tile<BM>(wi.tile, p.offsets, p.mstart, p.mtile, p.max_mt, p.G, p.rows, ntn);
     if (!tc.valid) return;
     const int n0 = tc.nt * BN;
     const int64_t K = p.K;
@@ -430,27 +430,42 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
         if (tid == 0) p.cnt[wi.unit] = 0;  // ready for the next launch
     }
 
-    // epilogue: accumulator r of a tile holds D[row][lane % MF] with
-    // row = 8*(r/4) + 4*(lane/32) + r%4 (32x32) or 4*(lane/16) + r (16x16)
+    // Epilogue: the activated tile goes through LDS (free after the K loop)
+    // so that the global stores are whole 16-byte chunks of rows.
+    // Accumulator r of an MFMA tile holds D[row][lane % MF] with
+    // row = 8*(r/4) + 4*(lane/32) + r%4 (32x32) or 4*(lane/16) + r (16x16).
+    // LDS: BM rows of BN bf16; 16-byte chunk c of row r at slot c ^ ((r/4) % 8),
+    // so the four row groups a store instruction writes hit distinct banks.
+    static_assert(BM * BN * 2 <= (int)sizeof(lds), "output tile fits in the staging buffers");
+    static_assert(BN % 64 == 0, "at least eight 16-byte chunks per output row");
+    constexpr int CPR = BN / 8;  // 16-byte chunks per output row
+    bf16 *Ct = &lds[0][0];
     const float *bias = p.bias ? p.bias + (int64_t)tc.g * p.N : nullptr;
+    __syncthreads();  // every wave is done with the operand tiles
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-            const int col = n0 + wn * WTN + j * MF + lane % MF;
-            if (col >= p.N) continue;
-            const float bcol = bias ? bias[col] : 0.f;
+            const int cl = wn * WTN + j * MF + lane % MF;  // column inside the tile
+            const float bcol = bias && n0 + cl < p.N ? bias[n0 + cl] : 0.f;
 #pragma unroll
             for (int r = 0; r < AR; ++r) {
                 const int rt = MF == 32 ? 8 * (r / 4) + 4 * (lane / 32) + r % 4 : 4 * (lane / 16) + r;
-                const int64_t row = tc.row0 + wm * WTM + i * MF + rt;
-                if (row >= tc.row_end) continue;
+                const int rl = wm * WTM + i * MF + rt;  // row inside the tile
                 float v = acc[i][j][r];
                 if constexpr (GLU) v = silu(v) * acc[i][TN + j][r];
                 else v = apply_act(p.act, v + bcol);
-                p.C[row * p.N + col] = (bf16)v;
+                Ct[rl * BN + (((cl / 8) ^ ((rl / 4) & 7)) * 8) + cl % 8] = (bf16)v;
             }
         }
+    __syncthreads();
+    for (int q = tid; q < BM * CPR; q += NT) {
+        const int rl = q / CPR, c = q % CPR;
+        const int64_t row = tc.row0 + rl;
+        const int col = n0 + c * 8;
+        if (row < tc.row_end && col < p.N)
+            store16(p.C + row * p.N + col, load16(Ct + rl * BN + ((c ^ ((rl / 4) & 7)) * 8)));
+    }
 }
 
 struct GemmParamsF32 {
@@ -461,6 +476,8 @@ struct GemmParamsF32 {
     float *C;
     const int32_t *offsets;
     const int32_t *mstart;
+    const int4 *mtile;
+    int max_mt;
     int G;
     int64_t rows;
     int N, K;
@@ -476,7 +493,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParamsF32 p) {
     __shared__ float Bs[BK][BN + 4];
     __shared__ float Bu[GLU ? BK : 1][BN + 4];
     const int ntn = (p.N + BN - 1) / BN;
-    const TileCoord tc = find_tile<BM>(xcd_remap(blockIdx.x), p.offsets, p.mstart, p.G, p.rows, ntn);
+    const TileCoord tc = find_tile<BM>(xcd_remap(blockIdx.x), p.offsets, p.mstart, p.mtile, p.max_mt, p.G, p.rows, ntn);
     if (!tc.valid) return;
     const int n0 = tc.nt * BN;
     const int64_t K = p.K;
@@ -537,30 +554,47 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParamsF32 p) {
 // ---------------------------------------------------------------------------
 // tile plan
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void tile_plan_kernel(const int32_t *__restrict__ counts, int E, int BM,
-                                                       int32_t *__restrict__ mstart, int32_t *__restrict__ cnt,
-                                                       int ncnt) {
-    const int lane = threadIdx.x;
-    for (int i = lane; i < ncnt; i += kWave) cnt[i] = 0;
-    int base = 0;
-    for (int e0 = 0; e0 < E; e0 += kWave) {
-        const int e = e0 + lane;
-        const int v = e < E ? (counts[e] + BM - 1) / BM : 0;
-        int incl = v;
+__global__ __launch_bounds__(256) void tile_plan_kernel(const int32_t *__restrict__ counts,
+                                                        const int32_t *__restrict__ offsets, int E, int BM,
+                                                        int32_t *__restrict__ mstart, int4 *__restrict__ mtile,
+                                                        int max_mt, int32_t *__restrict__ cnt, int ncnt) {
+    __shared__ int ms[kMaxPlanExperts + 1];
+    const int tid = threadIdx.x, lane = tid % kWave;
+    for (int i = tid; i < ncnt; i += 256) cnt[i] = 0;
+    if (tid < kWave) {
+        int base = 0;
+        for (int e0 = 0; e0 < E; e0 += kWave) {
+            const int e = e0 + lane;
+            const int v = e < E ? (counts[e] + BM - 1) / BM : 0;
+            int incl = v;
 #pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-            const int n = __shfl_up(incl, o, kWave);
-            if (lane >= o) incl += n;
+            for (int o = 1; o < kWave; o <<= 1) {
+                const int n = __shfl_up(incl, o, kWave);
+                if (lane >= o) incl += n;
+            }
+            if (e < E) {
+                mstart[e] = base + incl - v;
+                ms[e] = base + incl - v;
+            }
+            base += __shfl(incl, kWave - 1, kWave);
         }
-        if (e < E) mstart[e] = base + incl - v;
-        base += __shfl(incl, kWave - 1, kWave);
+        if (lane == 0) {
+            mstart[E] = base;
+            ms[E] = base;
+        }
     }
-    if (lane == 0) mstart[E] = base;
+    __syncthreads();
+    for (int e = tid; e < E; e += 256) {
+        const int first = ms[e], n = ms[e + 1] - first;
+        const int4 info = make_int4(first, e, offsets[e], offsets[e + 1]);
+        for (int m = 0; m < n && first + m < max_mt; ++m) mtile[first + m] = info;
+    }
 }
 
-void launch_tile_plan(const int32_t *counts, int E, int BM, int32_t *mstart, int32_t *cnt, int ncnt,
-                      hipStream_t s) {
-    hipLaunchKernelGGL(tile_plan_kernel, dim3(1), dim3(64), 0, s, counts, E, BM, mstart, cnt, cnt ? ncnt : 0);
+void launch_tile_plan(const int32_t *counts, const int32_t *offsets, int E, int BM, int32_t *mstart, int4 *mtile,
+                      int max_mt, int32_t *cnt, int ncnt, hipStream_t s) {
+    hipLaunchKernelGGL(tile_plan_kernel, dim3(1), dim3(256), 0, s, counts, offsets, E, BM, mstart, mtile, max_mt, cnt,
+                       cnt ? ncnt : 0);
 }
 
 int device_cus() {
@@ -602,7 +636,7 @@ static void launch_bf16_t(const GemmArgs &a, hipStream_t s) {
     static_assert((int64_t)BM * NB <= kSplitUnitFloats, "split-K unit");
     auto kern = gemm_bf16_kernel<BM, BN, WM, WN, GLU, FB, PD, SB, IL, MF, RMAP, GSKIP>;
     GemmParams p{(const bf16 *)a.A, (const bf16 *)a.B0, (const bf16 *)a.B1, a.bias, (bf16 *)a.C,
-                 a.offsets, a.mstart, a.G, a.rows, a.N, a.K, a.act, nullptr, nullptr, 0, 1};
+                 a.offsets, a.mstart, a.mtile, a.max_mt, a.G, a.rows, a.N, a.K, a.act, nullptr, nullptr, 0, 1};
     int64_t grid = grid_for(a, BM, BN);
     if (grid == 0) return;
     // Split K of the last round needs the number of co-resident workgroups
@@ -632,7 +666,7 @@ static void launch_bf16_t(const GemmArgs &a, hipStream_t s) {
 template <bool GLU>
 static void launch_f32_t(const GemmArgs &a, hipStream_t s) {
     GemmParamsF32 p{(const float *)a.A, (const float *)a.B0, (const float *)a.B1, a.bias, (float *)a.C,
-                    a.offsets, a.mstart, a.G, a.rows, a.N, a.K, a.act};
+                    a.offsets, a.mstart, a.mtile, a.max_mt, a.G, a.rows, a.N, a.K, a.act};
     const int64_t grid = grid_for(a, kF32BM, 64);
     if (grid == 0) return;
     hipLaunchKernelGGL((gemm_f32_kernel<GLU>), dim3((unsigned)grid), dim3(256), 0, s, p);

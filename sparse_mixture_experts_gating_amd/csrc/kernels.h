@@ -54,10 +54,15 @@ void launch_gather_rows(const void *x, const int32_t *row_token, const int32_t *
 
 // ---- expert FFN ----
 // Tile plan: mstart[e] = sum over experts e' < e of ceil(counts[e'] / BM), mstart[E] = total.
-// mstart[e] = first m-tile of expert e (exclusive scan of ceil(counts/BM));
-// also clears the split-K arrival counters cnt[0 .. ncnt) (cnt may be null).
-void launch_tile_plan(const int32_t *counts, int E, int BM, int32_t *mstart, int32_t *cnt, int ncnt,
-                      hipStream_t s);
+// mstart[e] = first m-tile of expert e (exclusive scan of ceil(counts/BM)),
+// mstart[E] = total; mtile[m] for every m-tile m < min(total, max_mt) =
+// {mstart[g], g, offsets[g], offsets[g+1]} of its expert g.  Also clears the split-K arrival counters cnt[0 .. ncnt) (cnt may
+// be null).  E <= kMaxPlanExperts.
+constexpr int kMaxPlanExperts = 1024;
+void launch_tile_plan(const int32_t *counts, const int32_t *offsets, int E, int BM, int32_t *mstart, int4 *mtile,
+                      int max_mt, int32_t *cnt, int ncnt, hipStream_t s);
+// capacity of the m-tile table for rows routed rows over E experts (any BM >= 32)
+inline int64_t max_mtiles(int64_t rows, int E) { return (rows + 31) / 32 + E; }
 
 // Split-K workspace of the bf16 grouped GEMM: float32 partial tiles of the
 // last, partial round of tiles plus one arrival counter per split tile.
@@ -79,6 +84,8 @@ struct GemmArgs {
     void *C;                // [rows][N] dtype
     const int32_t *offsets; // [G+1] or null: one group of `rows` rows
     const int32_t *mstart;  // [G+1] tile plan for the kernel's BM, or null with offsets null
+    const int4 *mtile;      // m-tile table of that plan, or null with offsets null
+    int max_mt;             // its capacity
     int G;                  // groups (experts)
     int64_t rows;           // rows of the single group when offsets is null; else A_max (grid bound)
     int N, K;

@@ -221,13 +221,15 @@ LossWs carve_losses(const Derived &D, Carve &c) {
 }
 
 struct FfnWs {
-    size_t mstart, h, hs, part, cnt;
+    size_t mstart, mtile, h, hs, part, cnt;
     int64_t part_floats;
-    int ncnt;
+    int ncnt, max_mt;
 };
 FfnWs carve_ffn(const Derived &D, Carve &c) {
     FfnWs w{};
     w.mstart = c.take((size_t)(D.E + 1) * 4);
+    w.max_mt = (int)max_mtiles(D.a_max, (int)D.E);
+    w.mtile = c.take((size_t)w.max_mt * 16);
     w.h = c.take((size_t)D.a_max * D.F * D.elem);
     w.hs = D.Fs ? c.take((size_t)D.T * D.Fs * D.elem) : 0;
     if (D.bf16) {
@@ -349,21 +351,24 @@ moe_status do_ffn(const Derived &D, const void *x_perm, const void *x, const moe
     void *H = ws + fw.h;
     const SplitKWs split{D.bf16 ? (float *)(ws + fw.part) : nullptr, fw.part_floats,
                          D.bf16 ? (int32_t *)(ws + fw.cnt) : nullptr, fw.ncnt};
-    TRY(launch(K_TILE_PLAN, s, [&] { launch_tile_plan(r->counts, (int)D.E, BM, mstart, split.cnt, split.ncnt, s); }));
-    GemmArgs g1{x_perm, w->w1, w->w3, w->b1, H, r->offsets, mstart, (int)D.E, D.a_max, (int)D.F, (int)D.d,
-                D.act == MOE_ACT_SWIGLU ? kActSwiglu : D.act, D.bf16, split};
+    int4 *mtile = (int4 *)(ws + fw.mtile);
+    TRY(launch(K_TILE_PLAN, s, [&] {
+        launch_tile_plan(r->counts, r->offsets, (int)D.E, BM, mstart, mtile, fw.max_mt, split.cnt, split.ncnt, s);
+    }));
+    GemmArgs g1{x_perm, w->w1, w->w3, w->b1, H, r->offsets, mstart, mtile, fw.max_mt, (int)D.E, D.a_max, (int)D.F,
+                (int)D.d, D.act == MOE_ACT_SWIGLU ? kActSwiglu : D.act, D.bf16, split};
     TRY(launch(K_GEMM1, s, [&] { launch_grouped_gemm(g1, shape, s); }));
-    GemmArgs g2{H, w->w2, nullptr, w->b2, y_perm, r->offsets, mstart, (int)D.E, D.a_max, (int)D.d, (int)D.F,
-                kActNone, D.bf16, split};
+    GemmArgs g2{H, w->w2, nullptr, w->b2, y_perm, r->offsets, mstart, mtile, fw.max_mt, (int)D.E, D.a_max, (int)D.d,
+                (int)D.F, kActNone, D.bf16, split};
     TRY(launch(K_GEMM2, s, [&] { launch_grouped_gemm(g2, shape, s); }));
     if (D.Fs) {
         const int sshape = D.T <= 32 ? kGemmDecode : kGemmPrefill;
         void *Hs = ws + fw.hs;
-        GemmArgs s1{x, w->ws1, w->ws3, nullptr, Hs, nullptr, nullptr, 1, D.T, (int)D.Fs, (int)D.d, kActSwiglu,
-                    D.bf16, split};
+        GemmArgs s1{x, w->ws1, w->ws3, nullptr, Hs, nullptr, nullptr, nullptr, 0, 1, D.T, (int)D.Fs, (int)D.d,
+                    kActSwiglu, D.bf16, split};
         TRY(launch(K_GEMM1_SHARED, s, [&] { launch_grouped_gemm(s1, sshape, s); }));
-        GemmArgs s2{Hs, w->ws2, nullptr, nullptr, y_shared, nullptr, nullptr, 1, D.T, (int)D.d, (int)D.Fs,
-                    kActNone, D.bf16, split};
+        GemmArgs s2{Hs, w->ws2, nullptr, nullptr, y_shared, nullptr, nullptr, nullptr, 0, 1, D.T, (int)D.d,
+                    (int)D.Fs, kActNone, D.bf16, split};
         TRY(launch(K_GEMM2_SHARED, s, [&] { launch_grouped_gemm(s2, sshape, s); }));
     }
     return MOE_OK;
