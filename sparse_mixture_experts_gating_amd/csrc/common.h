@@ -10,6 +10,7 @@ namespace moe {
 
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -74,6 +75,13 @@ __device__ inline float wave_max(float v) {
 }
 
 __device__ inline float silu(float z) { return z / (1.0f + expf(-z)); }
+// silu on the hardware transcendentals: e^-z = 2^(-z log2 e) (v_exp_f32) and
+// one reciprocal (v_rcp_f32), each about 1 ulp; for outputs rounded to bf16
+// (2^-9 relative) this matches the full-precision form.  Large negative z
+// gives 2^+inf = inf, rcp(inf) = 0, so the result tends to -0 as silu does.
+__device__ inline float silu_fast(float z) {
+    return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * 1.44269504088896341f));
+}
 __device__ inline float gelu_erf(float z) { return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f)); }
 
 __device__ inline float apply_act(int act, float z) {

@@ -433,14 +433,22 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
     // Epilogue: the activated tile goes through LDS (free after the K loop)
     // so that the global stores are whole 16-byte chunks of rows.
     // Accumulator r of an MFMA tile holds D[row][lane % MF] with
-    // row = 8*(r/4) + 4*(lane/32) + r%4 (32x32) or 4*(lane/16) + r (16x16).
-    // LDS: BM rows of BN bf16; 16-byte chunk c of row r at slot c ^ ((r/4) % 8),
-    // so the four row groups a store instruction writes hit distinct banks.
+    // row = 8*(r/4) + 4*(lane/32) + r%4 (32x32) or 4*(lane/16) + r (16x16):
+    // each group of four accumulators is four consecutive rows of one column.
+    // Lanes l and l^1 hold adjacent columns; they trade two values (DPP quad
+    // permutation 1,0,3,2) so that the even lane owns rows +0,+1 and the odd
+    // lane rows +2,+3 of both columns, and each writes bf16 pairs (4 bytes).
+    // LDS: BM rows of BN bf16; 16-byte chunk c of row r at slot c ^ ((r/2) % 8),
+    // so the eight rows one write instruction touches hit distinct banks.
     static_assert(BM * BN * 2 <= (int)sizeof(lds), "output tile fits in the staging buffers");
     static_assert(BN % 64 == 0, "at least eight 16-byte chunks per output row");
     constexpr int CPR = BN / 8;  // 16-byte chunks per output row
     bf16 *Ct = &lds[0][0];
     const float *bias = p.bias ? p.bias + (int64_t)tc.g * p.N : nullptr;
+    const bool odd = lane & 1;
+    auto swap1 = [](float x) {
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+    };
     __syncthreads();  // every wave is done with the operand tiles
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -449,13 +457,22 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
             const int cl = wn * WTN + j * MF + lane % MF;  // column inside the tile
             const float bcol = bias && n0 + cl < p.N ? bias[n0 + cl] : 0.f;
 #pragma unroll
-            for (int r = 0; r < AR; ++r) {
-                const int rt = MF == 32 ? 8 * (r / 4) + 4 * (lane / 32) + r % 4 : 4 * (lane / 16) + r;
-                const int rl = wm * WTM + i * MF + rt;  // row inside the tile
-                float v = acc[i][j][r];
-                if constexpr (GLU) v = silu(v) * acc[i][TN + j][r];
-                else v = apply_act(p.act, v + bcol);
-                Ct[rl * BN + (((cl / 8) ^ ((rl / 4) & 7)) * 8) + cl % 8] = (bf16)v;
+            for (int g = 0; g < AR / 4; ++g) {
+                float v[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    v[r] = acc[i][j][4 * g + r];
+                    if constexpr (GLU) v[r] = silu_fast(v[r]) * acc[i][TN + j][4 * g + r];
+                    else v[r] = apply_act(p.act, v[r] + bcol);
+                }
+                const float xs = swap1(odd ? v[0] : v[2]), ys = swap1(odd ? v[1] : v[3]);
+                const int rb = wm * WTM + i * MF + (MF == 32 ? 8 * g + 4 * (lane / 32) : 4 * (lane / 16));
+                const int ra0 = rb + (odd ? 2 : 0), ra1 = ra0 + 1;
+                const int ce = cl & ~1;  // even column of the pair
+                const bf16x2 p0 = {(bf16)(odd ? xs : v[0]), (bf16)(odd ? v[2] : xs)};
+                const bf16x2 p1 = {(bf16)(odd ? ys : v[1]), (bf16)(odd ? v[3] : ys)};
+                *(bf16x2 *)(Ct + ra0 * BN + (((ce / 8) ^ ((ra0 / 2) & 7)) * 8) + ce % 8) = p0;
+                *(bf16x2 *)(Ct + ra1 * BN + (((ce / 8) ^ ((ra1 / 2) & 7)) * 8) + ce % 8) = p1;
             }
         }
     __syncthreads();
@@ -464,7 +481,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
         const int64_t row = tc.row0 + rl;
         const int col = n0 + c * 8;
         if (row < tc.row_end && col < p.N)
-            store16(p.C + row * p.N + col, load16(Ct + rl * BN + ((c ^ ((rl / 4) & 7)) * 8)));
+            store16(p.C + row * p.N + col, load16(Ct + rl * BN + ((c ^ ((rl / 2) & 7)) * 8)));
     }
 }
 
