@@ -705,8 +705,12 @@ void launch_grouped_gemm(const GemmArgs &a, int shape, hipStream_t s) {
     // 32x32x16 on both GEMMs; row halves split across the two waves of a
     // SIMD (RMAP) 3% faster on the down projection and 1% slower on the
     // gate/up one; LDS reads interleaved 1:1 with the MFMAs (IL = 1) 2.5%
-    // faster on the down projection, no change on the gate/up one; the
-    // row-block skip of ragged tiles (GSKIP) 0.8% faster on the gate/up one.
+    // faster on the down projection, no change on the gate/up one.  The
+    // row-block skip of ragged tiles (GSKIP) lets tiles finish unevenly, which
+    // breaks the lock-step of a 32-tile XCD group and doubled the L2 misses
+    // (3.1 -> 6.5 GB on the Mixtral gate/up GEMM) for about 1% of time; it is
+    // used only when groups average fewer than four full tiles of rows, where
+    // most tiles are ragged (DeepSeek-style layers).
     if (shape == kGemmDecode) {
         if (glu) launch_bf16_t<32, 128, 1, 4, true, true, 2, false, 32>(a, s);
         else launch_bf16_t<32, 128, 1, 4, false, true, 2, false, 32>(a, s);
@@ -714,8 +718,13 @@ void launch_grouped_gemm(const GemmArgs &a, int shape, hipStream_t s) {
         if (glu) launch_bf16_t<128, 128, 2, 2, true, true, 2, true, 32>(a, s);
         else launch_bf16_t<128, 256, 2, 2, false, true, 2, true, 32>(a, s);
     } else {
-        if (glu) launch_bf16_t<256, 128, 2, 4, true, true, 2, false, 16, false, true, 0>(a, s);
-        else launch_bf16_t<256, 256, 2, 4, false, true, 2, false, 16, true, true, 1>(a, s);
+        if (a.ragged) {
+            if (glu) launch_bf16_t<256, 128, 2, 4, true, true, 2, false, 16, false, true, 0>(a, s);
+            else launch_bf16_t<256, 256, 2, 4, false, true, 2, false, 16, true, true, 1>(a, s);
+        } else {
+            if (glu) launch_bf16_t<256, 128, 2, 4, true, true, 2, false, 16, false, false, 0>(a, s);
+            else launch_bf16_t<256, 256, 2, 4, false, true, 2, false, 16, true, false, 1>(a, s);
+        }
     }
 }
 

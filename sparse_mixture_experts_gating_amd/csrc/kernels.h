@@ -92,6 +92,7 @@ struct GemmArgs {
     int act;                // ActKind; kActSwiglu uses B1
     bool bf16;
     SplitKWs split;         // bf16 only; part null = off
+    bool ragged;            // few rows per group on average: skip the MFMAs of row blocks past a group's end
 };
 enum GemmShape { kGemmPrefill = 0, kGemmSmallM = 1, kGemmDecode = 2 };
 int gemm_block_m(int shape, bool bf16);
