@@ -364,44 +364,85 @@ __device__ inline int block_exclusive_scan(int v, int *sh, int *total) {
     return base + incl - v;
 }
 
+// CACHE: the expert's column of logits (T <= kEcColMax) is read from global
+// memory once, with the stride E, into LDS, and every pass reads it there.
+// Histograms are per wave (atomics contend only inside a wave) and are
+// summed in wave order.
+constexpr int kEcColMax = 16384;
+template <bool CACHE>
 __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(const float *__restrict__ logits, int T, int E,
                                                                int C, int32_t *__restrict__ ec_idx,
                                                                float *__restrict__ ec_score) {
-    __shared__ float shf[kEcThreads / kWave];
-    __shared__ int shi[kEcThreads / kWave];
-    __shared__ uint32_t hist[256];
+    constexpr int NW = kEcThreads / kWave;
+    __shared__ float shf[NW];
+    __shared__ int shi[NW];
+    __shared__ uint32_t hist[NW][256];
     __shared__ uint32_t sel_prefix, sel_need;
     __shared__ uint64_t cand[kEcMaxCapacity];
+    __shared__ float colc[CACHE ? kEcColMax : 1];
     const int e = blockIdx.x;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, wave = tid / kWave;
     const float *col = logits + e;
+    if constexpr (CACHE) {
+        for (int t = tid; t < T; t += kEcThreads) colc[t] = col[(int64_t)t * E];
+        __syncthreads();
+    }
+    auto val = [&](int t) { return CACHE ? colc[t] : col[(int64_t)t * E]; };
 
     float m = -INFINITY;
-    for (int t = tid; t < T; t += kEcThreads) m = fmaxf(m, col[(int64_t)t * E]);
+    for (int t = tid; t < T; t += kEcThreads) m = fmaxf(m, val(t));
     m = block_reduce_max(m, shf);
     float z = 0.f;
-    for (int t = tid; t < T; t += kEcThreads) z += expf(col[(int64_t)t * E] - m);
+    for (int t = tid; t < T; t += kEcThreads) z += expf(val(t) - m);
     z = block_reduce_sum(z, shf);
 
     uint32_t prefix = 0, mask = 0, need = (uint32_t)C;
     for (int pass = 0; pass < 4; ++pass) {
         const int shift = 24 - 8 * pass;
-        for (int i = tid; i < 256; i += kEcThreads) hist[i] = 0;
+        for (int i = tid; i < NW * 256; i += kEcThreads) (&hist[0][0])[i] = 0;
         __syncthreads();
         for (int t = tid; t < T; t += kEcThreads) {
-            const uint32_t u = order_key(col[(int64_t)t * E]);
-            if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+            const uint32_t u = order_key(val(t));
+            if ((u & mask) == prefix) atomicAdd(&hist[wave][(u >> shift) & 255u], 1u);
         }
         __syncthreads();
-        if (tid == 0) {
-            uint32_t cum = 0;
-            int b = 255;
-            for (; b > 0; --b) {
-                if (cum + hist[b] >= need) break;
-                cum += hist[b];
+        for (int b = tid; b < 256; b += kEcThreads) {
+            uint32_t sum = 0;
+            for (int w = 0; w < NW; ++w) sum += hist[w][b];
+            hist[0][b] = sum;
+        }
+        __syncthreads();
+        if (wave == 0) {
+            // The bucket holding the `need`-th largest key: the first bucket,
+            // from the top, whose running count reaches `need` (bucket 0 if
+            // none among 255..1 does).  Lane l takes buckets 255-4l .. 252-4l;
+            // a wave prefix sum over the lanes' totals gives the running counts.
+            const int lane = tid;
+            uint32_t sq[4], acc4 = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                acc4 += hist[0][255 - (4 * lane + q)];
+                sq[q] = acc4;
             }
-            sel_need = need - cum;
-            sel_prefix = prefix | ((uint32_t)b << shift);
+            uint32_t incl = acc4;
+#pragma unroll
+            for (int o = 1; o < kWave; o <<= 1) {
+                const uint32_t nb = __shfl_up(incl, o, kWave);
+                if (lane >= o) incl += nb;
+            }
+            const uint32_t excl = incl - acc4;
+            int qsel = -1;
+#pragma unroll
+            for (int q = 3; q >= 0; --q)
+                if (4 * lane + q <= 254 && excl + sq[q] >= need) qsel = q;
+            const uint64_t hit = __ballot(qsel >= 0);
+            const int winner = hit ? __ffsll((unsigned long long)hit) - 1 : kWave - 1;
+            if (lane == winner) {
+                const int q = hit ? qsel : 3;
+                const uint32_t before = excl + (q == 0 ? 0u : q == 1 ? sq[0] : q == 2 ? sq[1] : sq[2]);
+                sel_need = need - before;
+                sel_prefix = prefix | ((uint32_t)(255 - (4 * lane + q)) << shift);
+            }
         }
         __syncthreads();
         need = sel_need;
@@ -417,7 +458,7 @@ __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(const float *__re
     const int t1 = min(T, t0 + chunk);
     int gt = 0, eq = 0;
     for (int t = t0; t < t1; ++t) {
-        const uint32_t u = order_key(col[(int64_t)t * E]);
+        const uint32_t u = order_key(val(t));
         gt += u > thr;
         eq += u == thr;
     }
@@ -425,7 +466,7 @@ __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(const float *__re
     int gt_base = block_exclusive_scan(gt, shi, &tot);
     int eq_base = block_exclusive_scan(eq, shi, &tot);
     for (int t = t0; t < t1; ++t) {
-        const float v = col[(int64_t)t * E];
+        const float v = val(t);
         const uint32_t u = order_key(v);
         if (u > thr) {
             if (gt_base < n_gt) cand[gt_base] = rank_key(v, (uint32_t)t);
@@ -660,7 +701,10 @@ void launch_gate_logits(const float *logits, int T, int E, int k, int gating, in
 
 void launch_ec_select(const float *logits, int T, int E, int C, int32_t *ec_idx, float *ec_score,
                       hipStream_t s) {
-    hipLaunchKernelGGL(ec_select_kernel, dim3(E), dim3(kEcThreads), 0, s, logits, T, E, C, ec_idx, ec_score);
+    if (T <= kEcColMax)
+        hipLaunchKernelGGL(ec_select_kernel<true>, dim3(E), dim3(kEcThreads), 0, s, logits, T, E, C, ec_idx, ec_score);
+    else
+        hipLaunchKernelGGL(ec_select_kernel<false>, dim3(E), dim3(kEcThreads), 0, s, logits, T, E, C, ec_idx, ec_score);
 }
 
 }  // namespace moe

@@ -52,7 +52,7 @@ def test_gate_from_logits_bit_exact(gating, E, k, ties):
 
 
 @pytest.mark.parametrize("ties", [False, True])
-@pytest.mark.parametrize("T,E", [(1000, 16), (8192, 64), (300, 7)])
+@pytest.mark.parametrize("T,E", [(1000, 16), (8192, 64), (300, 7), (16384, 4), (20000, 8)])  # > 16384: column not cached in LDS
 def test_expert_choice_select_bit_exact(T, E, ties):
     lg = workloads.random_logits(T, E, seed=200 + E, ties=ties)
     spec = workloads.LayerSpec("ec", 91, T=T, d=64, E=E, k=0, F=64, gating="expert_choice", act="swiglu",
