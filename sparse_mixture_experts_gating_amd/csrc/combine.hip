@@ -47,25 +47,53 @@ __device__ inline void store8<float>(float *p, const float *v) {
     store16(p + 4, b);
 }
 
+// The wave first compacts its token's kept slots (row >= 0) into LDS, in
+// slot order, with their gates; then, for each 8-element column chunk, it
+// issues the loads of up to kBatch kept rows at once and adds them in slot
+// order, so several loads are in flight per lane.
+constexpr int kMaxSlots = 1024;  // S <= E <= 1024
+constexpr int kBatch = 8;
 template <typename T>
 __global__ __launch_bounds__(256) void combine_kernel(const T *__restrict__ y_perm, const T *__restrict__ y_shared,
                                                       const float *__restrict__ w,
                                                       const int32_t *__restrict__ slot_row, int Tn, int d, int S,
                                                       int expert_choice, T *__restrict__ y) {
+    __shared__ int32_t krow[4][kMaxSlots];
+    __shared__ float kw[4][kMaxSlots];
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int64_t t = (int64_t)blockIdx.x * 4 + wave;
     if (t >= Tn) return;
     const int32_t *sr = slot_row + t * S;
+    int nv = 0;
+    for (int s0 = 0; s0 < S; s0 += kWave) {
+        const int s = s0 + lane;
+        const int row = s < S ? sr[s] : -1;
+        const bool keep = row >= 0;
+        const uint64_t m = __ballot(keep);
+        if (keep) {
+            const int pos = nv + __popcll(m & ((1ull << lane) - 1ull));
+            krow[wave][pos] = row;
+            kw[wave][pos] = expert_choice ? w[row] : w[t * S + s];
+        }
+        nv += __popcll(m);
+    }
+    // lanes read entries other lanes wrote: one wave's LDS operations execute
+    // in order, so only the compiler must not move the reads above the writes
+    __builtin_amdgcn_wave_barrier();
     for (int c0 = lane * 8; c0 < d; c0 += kWave * 8) {
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int s = 0; s < S; ++s) {
-            const int row = sr[s];
-            if (row < 0) continue;
-            const float g = expert_choice ? w[row] : w[t * S + s];
-            float v[8];
-            load8<T>(y_perm + (int64_t)row * d + c0, v);
+        for (int j0 = 0; j0 < nv; j0 += kBatch) {
+            float v[kBatch][8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] = fmaf(g, v[i], acc[i]);
+            for (int b = 0; b < kBatch; ++b)
+                if (j0 + b < nv) load8<T>(y_perm + (int64_t)krow[wave][j0 + b] * d + c0, v[b]);
+#pragma unroll
+            for (int b = 0; b < kBatch; ++b)
+                if (j0 + b < nv) {
+                    const float g = kw[wave][j0 + b];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) acc[i] = fmaf(g, v[b][i], acc[i]);
+                }
         }
         if (y_shared) {
             float v[8];
