@@ -78,43 +78,43 @@ __device__ void gate_one_token(const float *row, int E, int k, int gating, int64
     }
 }
 
-// Router GEMM on bf16 MFMA (v_mfma_f32_16x16x32_bf16) + gating epilogue, for
-// up to 64 experts.  A block owns 16*WM tokens; its 4 waves form WM (tokens)
-// x WK (K split) with WM*WK = 4.  Each wave computes 16 tokens x 16*NT experts over its K
-// range, straight from global memory (x rows are read once; the router
-// weights stay in L1/L2).  Partial sums meet in LDS in a fixed order, the
-// bias is added, logits are written, and each wave gates whole tokens.
+// Router GEMM on bf16 MFMA (v_mfma_f32_16x16x32_bf16) + gating epilogue for
+// few experts (16*NT at most; launched for up to 16).  A block owns 16 tokens
+// and its WK waves split the model dimension into WK contiguous ranges.  Each
+// wave computes 16 tokens x 16*NT experts over its range straight from global
+// memory, issuing U chunks of x and of the router weights before their MFMAs
+// so that enough bytes are in flight to stream x at HBM rate (x rows are read
+// once; the router weights stay in L1/L2).  Partial sums meet in LDS in a
+// fixed order, the bias is added, logits are written, and each wave gates
+// whole tokens.
 __device__ inline float softplus(float u) { return fmaxf(u, 0.f) + log1pf(expf(-fabsf(u))); }
 
 // NOISY adds the noise projection as a second MFMA accumulator set and forms
 // x.Wg + b + softplus(x.Wn) * noise ([yj-ja] TopKGating, training branch).
-template <int WM, int NT, bool NOISY>
-__global__ __launch_bounds__(256) void route_bf16_kernel(
+template <int NT, int WK, bool NOISY>
+__global__ __launch_bounds__(64 * WK) void route_bf16_kernel(
     const bf16 *__restrict__ x, const bf16 *__restrict__ wg, const float *__restrict__ bias,
     int T, int d, int E, int k, int gating, float *__restrict__ logits,
     int32_t *__restrict__ idx_out, float *__restrict__ w_out, const bf16 *__restrict__ wn,
     const float *__restrict__ noise) {
-    constexpr int WK = 4 / WM;
-    constexpr int TOK = 16 * WM;
+    constexpr int TOK = 16;
     constexpr int EP = 16 * NT;
     constexpr int LD = EP + 4;
+    constexpr int U = (NOISY ? 2 * NT : NT) <= 2 ? 8 : 4;  // chunks in flight per wave
     __shared__ float part[WK * TOK * LD];
     __shared__ float partn[NOISY ? WK * TOK * LD : 1];
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    const int wm = wave % WM, wk = wave / WM;
+    const int wk = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int64_t tok0 = (int64_t)blockIdx.x * TOK;
     const int r = lane % 16, kq = (lane / 16) * 8;
-    int64_t trow = tok0 + wm * 16 + r;
+    int64_t trow = tok0 + r;
     if (trow >= T) trow = T - 1;
     const bf16 *xa = x + trow * d + kq;
-    const bf16 *wb[NT];
     int64_t woff[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         int e = nt * 16 + r;
         if (e >= E) e = E - 1;
         woff[nt] = (int64_t)e * d + kq;
-        wb[nt] = wg + woff[nt];
     }
     f32x4 acc[NT], accn[NOISY ? NT : 1];
 #pragma unroll
@@ -124,28 +124,48 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(
     }
     const int nk = d / 32;
     const int kb = nk * wk / WK, ke = nk * (wk + 1) / WK;
-    for (int kc = kb; kc < ke; ++kc) {
+    auto step = [&](const bf16x8 &a, const bf16x8 *b, const bf16x8 *bn) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[nt], acc[nt], 0, 0, 0);
+            if constexpr (NOISY) accn[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bn[nt], accn[nt], 0, 0, 0);
+        }
+    };
+    int kc = kb;
+    for (; kc + U <= ke; kc += U) {
+        bf16x8 a[U], b[U][NT], bn[U][NOISY ? NT : 1];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            a[u] = __builtin_bit_cast(bf16x8, load16(xa + (kc + u) * 32));
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                b[u][nt] = __builtin_bit_cast(bf16x8, load16(wg + woff[nt] + (kc + u) * 32));
+                if constexpr (NOISY) bn[u][nt] = __builtin_bit_cast(bf16x8, load16(wn + woff[nt] + (kc + u) * 32));
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) step(a[u], b[u], bn[u]);
+    }
+    for (; kc < ke; ++kc) {
+        bf16x8 b[NT], bn[NOISY ? NT : 1];
         const bf16x8 a = __builtin_bit_cast(bf16x8, load16(xa + kc * 32));
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-            const bf16x8 b = __builtin_bit_cast(bf16x8, load16(wb[nt] + kc * 32));
-            acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[nt], 0, 0, 0);
-            if constexpr (NOISY) {
-                const bf16x8 bn = __builtin_bit_cast(bf16x8, load16(wn + woff[nt] + kc * 32));
-                accn[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bn, accn[nt], 0, 0, 0);
-            }
+            b[nt] = __builtin_bit_cast(bf16x8, load16(wg + woff[nt] + kc * 32));
+            if constexpr (NOISY) bn[nt] = __builtin_bit_cast(bf16x8, load16(wn + woff[nt] + kc * 32));
         }
+        step(a, b, bn);
     }
     // D[row = 4*(lane/16) + j][col = lane%16] of each 16x16 tile
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            part[(wk * TOK + wm * 16 + 4 * (lane / 16) + j) * LD + nt * 16 + r] = acc[nt][j];
-            if constexpr (NOISY) partn[(wk * TOK + wm * 16 + 4 * (lane / 16) + j) * LD + nt * 16 + r] = accn[nt][j];
+            part[(wk * TOK + 4 * (lane / 16) + j) * LD + nt * 16 + r] = acc[nt][j];
+            if constexpr (NOISY) partn[(wk * TOK + 4 * (lane / 16) + j) * LD + nt * 16 + r] = accn[nt][j];
         }
     __syncthreads();
-    for (int i = threadIdx.x; i < TOK * EP; i += 256) {
+    for (int i = threadIdx.x; i < TOK * EP; i += 64 * WK) {
         const int tt = i / EP, e = i % EP;
         float s = part[tt * LD + e];
 #pragma unroll
@@ -165,7 +185,7 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(
     }
     __syncthreads();
     if (gating == kGateExpertChoice) return;
-    for (int tt = wave; tt < TOK; tt += 4) {
+    for (int tt = wk; tt < TOK; tt += WK) {
         const int64_t t = tok0 + tt;
         if (t < T) gate_one_token(part + tt * LD, E, k, gating, t, idx_out, w_out);
     }
@@ -653,22 +673,31 @@ static void launch_router_tile_t(const RouteArgs &a, hipStream_t s) {
 
 template <int TOK>
 static void launch_router_tile(const RouteArgs &a, hipStream_t s) {
-    if (a.E <= 128) launch_router_tile_t<TOK, 128>(a, s);
+    if (a.E <= 64) launch_router_tile_t<TOK, 64>(a, s);
+    else if (a.E <= 128) launch_router_tile_t<TOK, 128>(a, s);
     else launch_router_tile_t<TOK, 256>(a, s);
 }
 
-template <int WM, int NT>
-static void launch_route_bf16_t(const RouteArgs &a, hipStream_t s) {
-    const int tok = 16 * WM;
-    const int grid = (a.T + tok - 1) / tok;
+template <int NT, int WK>
+static void launch_route_bf16_wk(const RouteArgs &a, hipStream_t s) {
+    const int grid = (a.T + 15) / 16;
     if (a.wn)
-        hipLaunchKernelGGL((route_bf16_kernel<WM, NT, true>), dim3(grid), dim3(256), 0, s, (const bf16 *)a.x,
+        hipLaunchKernelGGL((route_bf16_kernel<NT, WK, true>), dim3(grid), dim3(64 * WK), 0, s, (const bf16 *)a.x,
                            (const bf16 *)a.wg, a.bias, a.T, a.d, a.E, a.k, a.gating, a.logits, a.idx, a.w,
                            (const bf16 *)a.wn, a.noise);
     else
-        hipLaunchKernelGGL((route_bf16_kernel<WM, NT, false>), dim3(grid), dim3(256), 0, s, (const bf16 *)a.x,
+        hipLaunchKernelGGL((route_bf16_kernel<NT, WK, false>), dim3(grid), dim3(64 * WK), 0, s, (const bf16 *)a.x,
                            (const bf16 *)a.wg, a.bias, a.T, a.d, a.E, a.k, a.gating, a.logits, a.idx, a.w,
                            nullptr, nullptr);
+}
+
+// K-split depth: 16 waves once each holds at least eight 32-wide chunks.
+template <int NT>
+static void launch_route_bf16_t(const RouteArgs &a, hipStream_t s) {
+    const int nk = a.d / 32;
+    if (nk >= 128) launch_route_bf16_wk<NT, 16>(a, s);
+    else if (nk >= 32) launch_route_bf16_wk<NT, 8>(a, s);
+    else launch_route_bf16_wk<NT, 4>(a, s);
 }
 
 void launch_route(const RouteArgs &a, hipStream_t s) {
@@ -679,13 +708,11 @@ void launch_route(const RouteArgs &a, hipStream_t s) {
                            (const float *)a.wn, a.noise);
         return;
     }
-    // More than 64 experts: LDS-staged tiles (the weight rows are shared by
-    // a block's tokens); up to 64, per-wave K slices straight from global
-    // memory, which measured faster for few experts.
-    if (a.E <= 64) {
-        if (a.E <= 16) launch_route_bf16_t<1, 1>(a, s);
-        else if (a.E <= 32) launch_route_bf16_t<1, 2>(a, s);
-        else launch_route_bf16_t<1, 4>(a, s);
+    // Up to 16 experts: per-wave K slices straight from global memory.  More
+    // experts: LDS-staged tiles, so that a block's tokens share each weight
+    // row instead of every 16-token wave re-reading all of them from L2.
+    if (a.E <= 16) {
+        launch_route_bf16_t<1>(a, s);
         return;
     }
     // 32-token blocks unless that already gives a block per CU twice over
