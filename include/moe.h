@@ -215,7 +215,10 @@ moe_status moe_combine(const moe_config *cfg, const void *y_perm, const void *y_
 
 /* The whole layer: route -> permute -> expert_ffn -> combine, no host
  * synchronisation.  routing may be NULL (all routing buffers in ws) or a
- * caller-owned set that receives the routing.  ws: MOE_STAGE_FORWARD bytes. */
+ * caller-owned set that receives the routing.  ws: MOE_STAGE_FORWARD bytes.
+ * With bf16 data and T*d*2 < 2^31 the first expert GEMM reads the routed rows
+ * of x through routing.row_token instead of a gathered x_perm (same values,
+ * same result). */
 moe_status moe_forward(const moe_config *cfg, const void *x, const moe_weights *w, void *y,
                        moe_routing *routing, void *ws, size_t ws_bytes, void *stream);
 

@@ -103,6 +103,10 @@ struct GemmParams {
     int32_t *cnt;     // [slots] arrival counters, zero between launches
     int slots;        // workgroups resident at once (one per CU)
     int max_split;    // at most this many K parts per tile
+    // gathered A: row r of the grouped operand is row arow[r] of A, whose
+    // a_bytes bytes one buffer resource covers (null: rows in place)
+    const int32_t *arow;
+    int64_t a_bytes;
 };
 
 // Work item of one workgroup.  The tiles fill rounds of `slots` workgroups;
@@ -223,15 +227,22 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
     // tid/8 + RSTEP*i.
     const int r0 = tid / 8, ch0 = tid % 8;
     const int64_t k0 = (int64_t)kbeg * BK;
-    const char *abase = (const char *)(p.A + tc.row0 * K + k0);
+    // Gathered A: one resource over all of A and a per-row byte offset from
+    // the row map; padding rows get an offset past the limit (zeros).
+    const char *abase = p.arow ? (const char *)(p.A + k0) : (const char *)(p.A + tc.row0 * K + k0);
     const char *b0base = (const char *)(p.B0 + ((int64_t)tc.g * p.N + n0) * K + k0);
     const char *b1base = GLU ? (const char *)(p.B1 + ((int64_t)tc.g * p.N + n0) * K + k0) : nullptr;
-    const __amdgpu_buffer_rsrc_t arsrc = buffer_rsrc(abase, (tc.row_end - tc.row0) * K * 2);
+    const __amdgpu_buffer_rsrc_t arsrc =
+        buffer_rsrc(abase, p.arow ? p.a_bytes - k0 * 2 : (tc.row_end - tc.row0) * K * 2);
     const __amdgpu_buffer_rsrc_t b0rsrc = buffer_rsrc(b0base, (int64_t)(p.N - n0) * K * 2);
     const __amdgpu_buffer_rsrc_t b1rsrc = GLU ? buffer_rsrc(b1base, (int64_t)(p.N - n0) * K * 2) : b0rsrc;
     uint32_t aoff[A_PER_T], boff[B_PER_T];
 #pragma unroll
-    for (int i = 0; i < A_PER_T; ++i) aoff[i] = (uint32_t)(((r0 + RSTEP * i) * K + ch0 * 8) * 2);
+    for (int i = 0; i < A_PER_T; ++i) {
+        const int64_t r = r0 + RSTEP * i;
+        if (p.arow == nullptr) aoff[i] = (uint32_t)((r * K + ch0 * 8) * 2);
+        else aoff[i] = (tc.row0 + r < tc.row_end ? (uint32_t)(p.arow[tc.row0 + r] * K * 2) : 0x80000000u) + ch0 * 16;
+    }
 #pragma unroll
     for (int i = 0; i < B_PER_T; ++i) {
         int r = r0 + RSTEP * i;
@@ -653,7 +664,8 @@ static void launch_bf16_t(const GemmArgs &a, hipStream_t s) {
     static_assert((int64_t)BM * NB <= kSplitUnitFloats, "split-K unit");
     auto kern = gemm_bf16_kernel<BM, BN, WM, WN, GLU, FB, PD, SB, IL, MF, RMAP, GSKIP>;
     GemmParams p{(const bf16 *)a.A, (const bf16 *)a.B0, (const bf16 *)a.B1, a.bias, (bf16 *)a.C,
-                 a.offsets, a.mstart, a.mtile, a.max_mt, a.G, a.rows, a.N, a.K, a.act, nullptr, nullptr, 0, 1};
+                 a.offsets, a.mstart, a.mtile, a.max_mt, a.G, a.rows, a.N, a.K, a.act, nullptr, nullptr, 0, 1,
+                 a.arow, a.a_rows * a.K * 2};
     int64_t grid = grid_for(a, BM, BN);
     if (grid == 0) return;
     // Split K of the last round needs the number of co-resident workgroups

@@ -93,6 +93,11 @@ struct GemmArgs {
     bool bf16;
     SplitKWs split;         // bf16 only; part null = off
     bool ragged;            // few rows per group on average: skip the MFMAs of row blocks past a group's end
+    // bf16 only: A holds a_rows source rows, and row r of the grouped
+    // operand is A row arow[r] (the routed token rows, gathered by the tile
+    // loads themselves).  Needs a_rows * K * 2 < 2^31.
+    const int32_t *arow = nullptr;
+    int64_t a_rows = 0;
 };
 enum GemmShape { kGemmPrefill = 0, kGemmSmallM = 1, kGemmDecode = 2 };
 int gemm_block_m(int shape, bool bf16);

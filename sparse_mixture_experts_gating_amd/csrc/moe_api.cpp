@@ -308,7 +308,7 @@ moe_status do_route(const Derived &D, const void *x, const moe_weights *w, const
 }
 
 moe_status do_permute(const Derived &D, const void *x, const moe_routing *r, void *x_perm, char *ws,
-                      const PermuteWs &pw, hipStream_t s) {
+                      const PermuteWs &pw, hipStream_t s, bool gather = true) {
     if (D.T == 0) return MOE_OK;
     if (D.ec) {
         TRY(launch(K_EC_PERMUTE, s, [&] {
@@ -323,11 +323,17 @@ moe_status do_permute(const Derived &D, const void *x, const moe_routing *r, voi
         TRY(launch(K_PERM_SCAN, s, [&] { launch_permute_scan(a, s); }));
         TRY(launch(K_PERM_SCATTER, s, [&] { launch_permute_scatter(a, s); }));
     }
-    TRY(launch(K_GATHER, s, [&] {
-        launch_gather_rows(x, r->row_token, r->offsets, (int)D.E, D.a_max, (int)D.d, (int)D.elem, x_perm, s);
-    }));
+    if (gather)
+        TRY(launch(K_GATHER, s, [&] {
+            launch_gather_rows(x, r->row_token, r->offsets, (int)D.E, D.a_max, (int)D.d, (int)D.elem, x_perm, s);
+        }));
     return MOE_OK;
 }
+
+// The forward pass skips the gather kernel when the first GEMM can load the
+// routed token rows itself: bf16 (the grouped MFMA kernel) and all of x
+// addressable by one buffer resource (32-bit byte offsets below 2^31).
+bool gather_in_gemm(const Derived &D) { return D.bf16 && (int64_t)D.T * D.d * 2 <= 0x7fffffff; }
 
 int pick_shape(const Derived &D) {
     if (D.ec) return D.capacity <= 160 ? kGemmSmallM : kGemmPrefill;
@@ -342,6 +348,8 @@ int pick_shape(const Derived &D) {
     return kGemmPrefill;
 }
 
+// x_perm null: the first GEMM reads the routed rows straight from x through
+// the row map (bf16, x within one buffer resource; see gather_in_gemm).
 moe_status do_ffn(const Derived &D, const void *x_perm, const void *x, const moe_routing *r, const moe_weights *w,
                   void *y_perm, void *y_shared, char *ws, const FfnWs &fw, hipStream_t s) {
     if (D.T == 0) return MOE_OK;
@@ -359,6 +367,11 @@ moe_status do_ffn(const Derived &D, const void *x_perm, const void *x, const moe
     const bool ragged = D.a_max < 4 * 256 * D.E;
     GemmArgs g1{x_perm, w->w1, w->w3, w->b1, H, r->offsets, mstart, mtile, fw.max_mt, (int)D.E, D.a_max, (int)D.F,
                 (int)D.d, D.act == MOE_ACT_SWIGLU ? kActSwiglu : D.act, D.bf16, split, ragged};
+    if (x_perm == nullptr) {
+        g1.A = x;
+        g1.arow = r->row_token;
+        g1.a_rows = D.T;
+    }
     TRY(launch(K_GEMM1, s, [&] { launch_grouped_gemm(g1, shape, s); }));
     GemmArgs g2{H, w->w2, nullptr, w->b2, y_perm, r->offsets, mstart, mtile, fw.max_mt, (int)D.E, D.a_max, (int)D.d,
                 (int)D.F, kActNone, D.bf16, split, ragged};
@@ -604,8 +617,9 @@ moe_status moe_forward(const moe_config *cfg, const void *x, const moe_weights *
     void *y_perm = base + fw.y_perm;
     void *y_shared = D.Fs ? base + fw.y_shared : nullptr;
     TRY(do_route(D, x, w, &r, s));
-    TRY(do_permute(D, x, &r, x_perm, base, fw.perm, s));
-    TRY(do_ffn(D, x_perm, x, &r, w, y_perm, y_shared, base, fw.ffn, s));
+    const bool fused = gather_in_gemm(D);
+    TRY(do_permute(D, x, &r, x_perm, base, fw.perm, s, !fused));
+    TRY(do_ffn(D, fused ? nullptr : x_perm, x, &r, w, y_perm, y_shared, base, fw.ffn, s));
     return do_combine(D, y_perm, y_shared, &r, y, s);
 }
 

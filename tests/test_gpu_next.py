@@ -141,3 +141,26 @@ def test_noisy_forward_matches_oracle(spec):
     dl = np.abs(_np(routing["logits"]).astype(np.float64) - ref["logits"]).max()
     assert dl <= 1e-3 * np.abs(ref["logits"]).max()
     _check_layer(spec, inp, y, routing, ref)
+
+
+# The forward pass loads the routed token rows inside the first GEMM (bf16);
+# the step entry points gather them into x_perm first.  Same products in the
+# same order: the outputs agree bit for bit.
+GATHER_SPECS = [s for s in workloads.SMALL if s.dtype == "bf16"] + [
+    workloads.MIXTRAL_PREFILL_BF16.replace(name="fused_gather_split_k", T=700, d=4096, F=256),
+    workloads.MIXTRAL_PREFILL_BF16.replace(name="fused_gather_small_m", T=300, d=2048, F=512),
+    workloads.MIXTRAL_DECODE_BF16.replace(name="fused_gather_decode", d=512, F=1024),
+    workloads.SWITCH_TOP1_BF16.replace(name="fused_gather_drops", T=1000, d=256, F=512),
+]
+
+
+@pytest.mark.parametrize("spec", GATHER_SPECS, ids=lambda s: s.name)
+def test_forward_gather_in_gemm_equals_step_path(spec):
+    from gpu_harness import run_forward
+    dinp = to_dev(workloads.make_inputs(spec))
+    y_fwd, r_fwd = run_forward(spec, dinp)
+    y_steps, r_steps = _run_steps(spec, dinp, noisy=False)
+    n = int(r_fwd["offsets"][-1])  # rows past the kept ones are unspecified
+    assert torch.equal(r_fwd["offsets"], r_steps["offsets"])
+    assert torch.equal(r_fwd["row_token"][:n], r_steps["row_token"][:n])
+    assert torch.equal(y_fwd, y_steps)
