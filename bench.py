@@ -39,19 +39,60 @@ def active_flops(spec, counts):
     return router + experts + shared
 
 
-def gemm1_flops(spec, rows):
-    per_row = 2.0 * spec.d * spec.F * (2 if spec.act == "swiglu" else 1)
-    return rows * per_row
-
-
-def gemm1_bytes(spec, counts):
-    """Algorithmic bytes of the first grouped GEMM: the routed rows once, the
-    weights of every expert that received rows once, the hidden rows once."""
+def kernel_work(spec, counts, name):
+    """Algorithmic (flops, HBM bytes) of one step's launches of kernel `name`:
+    what the step must compute, read and write once (x once, the weights of
+    every expert that received rows once, each intermediate written and read
+    once, routing metadata); re-reads caused by tiling are not counted."""
     eb = 2 if spec.dtype == "bf16" else 4
+    T, d, E, F, Fs = spec.T, spec.d, spec.E, spec.F, spec.F_shared
+    ec = spec.gating == "expert_choice"
+    rows = float(sum(counts))                      # kept (routed) rows
+    touched = sum(1 for c in counts if c > 0)      # experts that received rows
+    slots = rows if ec else float(T * spec.k)      # gate slots the combine walks
     nw = 2 if spec.act == "swiglu" else 1
-    rows = float(sum(counts))
-    touched = sum(1 for c in counts if c > 0)
-    return eb * (rows * spec.d + touched * nw * spec.F * spec.d + rows * spec.F)
+    if name == "route":
+        return 2.0 * T * d * E, eb * (T * d + E * d) + 4.0 * T * E + (0.0 if ec else 8.0 * T * spec.k)
+    if name == "ec_select":
+        return 0.0, 4.0 * T * E + 8.0 * rows
+    if name == "permute_count":
+        return 0.0, 4.0 * slots + 4.0 * E
+    if name == "permute_scan":
+        return 0.0, 12.0 * E
+    if name == "permute_small":
+        return 0.0, 8.0 * slots + 4.0 * rows + 8.0 * E
+    if name == "permute_scatter":
+        return 0.0, 8.0 * slots + 4.0 * rows
+    if name == "ec_permute":
+        return 0.0, 4.0 * rows + 4.0 * T * E + 4.0 * rows
+    if name == "gather_rows":
+        return 0.0, 2.0 * eb * rows * d
+    if name == "tile_plan":
+        return 0.0, 8.0 * E
+    if name == "gemm1_act":
+        return 2.0 * rows * d * F * nw, eb * (rows * d + touched * nw * F * d + rows * F)
+    if name == "gemm2":
+        return 2.0 * rows * F * d, eb * (rows * F + touched * d * F + rows * d)
+    if name == "gemm1_act_shared":
+        return 4.0 * T * d * Fs, eb * (T * d + 2.0 * Fs * d + T * Fs)
+    if name == "gemm2_shared":
+        return 2.0 * T * Fs * d, eb * (T * Fs + d * Fs + T * d)
+    if name == "combine":
+        meta = 4.0 * T * E if ec else 8.0 * slots
+        return 0.0, eb * (rows * d + T * d + (T * d if Fs else 0.0)) + meta
+    return 0.0, 0.0
+
+
+def kernel_roofline(spec, flops, nbytes, seconds):
+    """Bound from the arithmetic intensity against the ridge point (peak
+    flops / peak HBM bandwidth); launch-latency for kernels that move under a
+    megabyte and do no matrix work.  Returns (bound, achieved, peak, unit)."""
+    peak_f = PEAK_BF16_TFLOPS if spec.dtype == "bf16" else PEAK_F32_TFLOPS
+    ridge = peak_f * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if flops > 0 and flops / max(nbytes, 1.0) >= ridge:
+        return "mfma", flops / seconds / 1e12, peak_f, "TFLOP/s"
+    bound = "hbm" if (flops > 0 or nbytes >= 1e6) else "latency"
+    return bound, nbytes / seconds / 1e9, PEAK_HBM_GBS, "GB/s"
 
 
 GEMM_SOURCES = ("gemm.hip", "common.h", "kernels.h")
@@ -155,29 +196,40 @@ def main():
         if cnt:
             kern[n] = dict(avg_us=round(tot * 1e3 / cnt, 3), launches_per_step=cnt / args.steps)
     moe.moe_timing_enable(False)
+    # per-kernel rooflines: algorithmic work per step over the kernel's time per step
+    for n, v in kern.items():
+        fl, nb = kernel_work(spec, counts, n)
+        per_step_s = v["avg_us"] * v["launches_per_step"] * 1e-6
+        bound, ach, peak, unit = kernel_roofline(spec, fl, nb, per_step_s)
+        v.update(gflop=round(fl / 1e9, 3), mbytes=round(nb / 1e6, 3), bound=bound, achieved=round(ach, 2),
+                 unit=unit, frac=round(ach / peak, 4))
     dominant = max(kern, key=lambda n: kern[n]["avg_us"] * kern[n]["launches_per_step"])
-    avg_s = kern[dominant]["avg_us"] * 1e-6
-    if dominant == "gemm1_act":
-        ach = gemm1_flops(spec, sum(counts)) / avg_s / 1e12
-        bound = "mfma"
-        peak = PEAK_BF16_TFLOPS if spec.dtype == "bf16" else PEAK_F32_TFLOPS
-        unit = "TFLOP/s"
-    elif dominant == "gemm2":
-        ach = gemm1_flops(spec, sum(counts)) / (2 if spec.act == "swiglu" else 1) / avg_s / 1e12
-        bound = "mfma"
-        peak = PEAK_BF16_TFLOPS if spec.dtype == "bf16" else PEAK_F32_TFLOPS
-        unit = "TFLOP/s"
-    else:
-        ach, bound, peak, unit = None, "hbm", PEAK_HBM_GBS, "GB/s"
+    dk = kern[dominant]
     traffic = measured_traffic(spec.name, dominant)
-    roofline = dict(bound=bound, kernel=dominant, achieved=None if ach is None else round(ach, 2), peak=peak,
-                    unit=unit, frac=None if ach is None else round(ach / peak, 4),
-                    traffic=None if traffic is None else traffic["bytes"],
-                    avg_launch_us=kern[dominant]["avg_us"])
+    roofline = dict(bound=dk["bound"], kernel=dominant, achieved=dk["achieved"],
+                    peak=PEAK_HBM_GBS if dk["unit"] == "GB/s" else
+                    (PEAK_BF16_TFLOPS if spec.dtype == "bf16" else PEAK_F32_TFLOPS),
+                    unit=dk["unit"], frac=dk["frac"], traffic=None if traffic is None else traffic["bytes"],
+                    avg_launch_us=dk["avg_us"])
     if traffic is not None:
-        alg = gemm1_bytes(spec, counts) if dominant == "gemm1_act" else None
         roofline["traffic_detail"] = dict(unit="bytes per launch", read=traffic["read"], written=traffic["written"],
-                                          algorithmic=alg, source="profiles/hbm_traffic_mixtral_prefill.md")
+                                          algorithmic=round(dk["mbytes"] * 1e6 / dk["launches_per_step"]),
+                                          source="profiles/hbm_traffic_mixtral_prefill.md")
+
+    # cold-cache step: the 256 MB MALL is overwritten by a 512 MiB fill before
+    # each step, outside the event pair
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold = []
+    for _ in range(max(3, min(args.steps, 10))):
+        flush.fill_(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        e1.synchronize()
+        cold.append(e0.elapsed_time(e1))
+    del flush
+    cold_ms = float(np.median(cold))
 
     if args.copy_probe_mib:
         n = args.copy_probe_mib * (1 << 20)
@@ -208,7 +260,9 @@ def main():
                    "activation": spec.act, "parallelism": "none (1 GPU)"},
         "layer_tflops_active": round(layer_tflops, 2),
         "layer_frac_bf16_peak": round(layer_tflops / PEAK_BF16_TFLOPS, 4),
+        "cold_ms_per_step": round(cold_ms, 4),
         "kernels_us": {n: v["avg_us"] for n, v in kern.items()},
+        "kernels": kern,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

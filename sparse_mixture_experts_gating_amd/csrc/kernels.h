@@ -44,6 +44,14 @@ struct PermuteArgs {
     int32_t *ranks;      // [T][k]
     int32_t *counts, *offsets, *row_token, *slot_row;
 };
+// One-workgroup permutation (count, scan and scatter in LDS) for batches whose
+// chunk tables fit: E <= kMaxSmallExperts, nc * E * 16 <= kSmallLdsBytes and
+// T * k <= kSmallMaxSlots.  Writes counts, offsets, row_token and slot_row.
+constexpr int kMaxSmallExperts = 1024;
+constexpr int kSmallLdsBytes = 48 * 1024;
+constexpr int kSmallMaxSlots = 16384;
+bool permute_small_fits(int T, int E, int k);
+void launch_permute_small(const PermuteArgs &a, hipStream_t s);
 void launch_permute_count(const PermuteArgs &a, hipStream_t s);
 void launch_permute_scan(const PermuteArgs &a, hipStream_t s);
 void launch_permute_scatter(const PermuteArgs &a, hipStream_t s);

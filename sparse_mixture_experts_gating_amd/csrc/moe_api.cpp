@@ -34,11 +34,12 @@ moe_status fail(moe_status st, const char *fmt, ...) {
 // ---------------------------------------------------------------------------
 enum Kind {
     K_ROUTE, K_GATE_LOGITS, K_EC_SELECT, K_PERM_COUNT, K_PERM_SCAN, K_PERM_SCATTER, K_EC_PERMUTE, K_GATHER,
-    K_TILE_PLAN, K_GEMM1, K_GEMM2, K_GEMM1_SHARED, K_GEMM2_SHARED, K_COMBINE, K_ROUTER_STATS, K_COUNT
+    K_TILE_PLAN, K_GEMM1, K_GEMM2, K_GEMM1_SHARED, K_GEMM2_SHARED, K_COMBINE, K_ROUTER_STATS, K_PERM_SMALL, K_COUNT
 };
 const char *kKindNames[K_COUNT] = {"route", "gate_logits", "ec_select", "permute_count", "permute_scan",
                                    "permute_scatter", "ec_permute", "gather_rows", "tile_plan", "gemm1_act",
-                                   "gemm2", "gemm1_act_shared", "gemm2_shared", "combine", "router_stats"};
+                                   "gemm2", "gemm1_act_shared", "gemm2_shared", "combine", "router_stats",
+                                   "permute_small"};
 
 struct Pending {
     hipEvent_t a, b;
@@ -319,9 +320,13 @@ moe_status do_permute(const Derived &D, const void *x, const moe_routing *r, voi
         PermuteArgs a{r->topk_idx, (int)D.T, (int)D.E, (int)D.k, D.capacity, D.group_chunks,
                       (int32_t *)(ws + pw.counts), (int32_t *)(ws + pw.pre), (int32_t *)(ws + pw.base),
                       (int32_t *)(ws + pw.ranks), r->counts, r->offsets, r->row_token, r->slot_row};
-        TRY(launch(K_PERM_COUNT, s, [&] { launch_permute_count(a, s); }));
-        TRY(launch(K_PERM_SCAN, s, [&] { launch_permute_scan(a, s); }));
-        TRY(launch(K_PERM_SCATTER, s, [&] { launch_permute_scatter(a, s); }));
+        if (permute_small_fits((int)D.T, (int)D.E, (int)D.k)) {
+            TRY(launch(K_PERM_SMALL, s, [&] { launch_permute_small(a, s); }));
+        } else {
+            TRY(launch(K_PERM_COUNT, s, [&] { launch_permute_count(a, s); }));
+            TRY(launch(K_PERM_SCAN, s, [&] { launch_permute_scan(a, s); }));
+            TRY(launch(K_PERM_SCATTER, s, [&] { launch_permute_scatter(a, s); }));
+        }
     }
     if (gather)
         TRY(launch(K_GATHER, s, [&] {

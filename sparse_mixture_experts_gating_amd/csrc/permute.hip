@@ -143,6 +143,111 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(const int32_t *__r
     row_token[row] = (int32_t)t;
 }
 
+// ---------------------------------------------------------------------------
+// Small batches: the three phases above in one workgroup, with the per-chunk
+// masks, prefixes and bases in LDS (nc * E * 16 bytes), so a decode-sized or
+// mid-sized batch pays one launch instead of three.  Same formulas, so the
+// same counts, offsets, rows and drops.
+// ---------------------------------------------------------------------------
+constexpr int kSmallThreads = 1024;
+
+__global__ __launch_bounds__(kSmallThreads) void permute_small_kernel(const int32_t *__restrict__ idx, int T, int E,
+                                                                      int k, int capacity, int group_chunks,
+                                                                      int32_t *__restrict__ counts,
+                                                                      int32_t *__restrict__ offsets,
+                                                                      int32_t *__restrict__ row_token,
+                                                                      int32_t *__restrict__ slot_row) {
+    extern __shared__ unsigned long long lds_u64[];
+    const int nc = (T + kChunk - 1) / kChunk;
+    unsigned long long *masks = lds_u64;                   // [nc][E]
+    int32_t *pre = (int32_t *)(masks + (int64_t)nc * E);  // [nc][E] in-group prefix before the chunk
+    int32_t *base = pre + (int64_t)nc * E;                  // [nc][E] kept rows of e before the chunk
+    __shared__ int wsum[kSmallThreads / kWave];
+    __shared__ int offs[kMaxSmallExperts + 1];
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    for (int i = tid; i < nc * E; i += kSmallThreads) masks[i] = 0ull;
+    __syncthreads();
+    // chunk masks: bit l of masks[c][e] = token 64c + l chose e
+    for (int c = wave; c < nc; c += kSmallThreads / kWave) {
+        const int t = c * kChunk + lane;
+        if (t < T)
+            for (int j = 0; j < k; ++j) {
+                const int e = idx[(int64_t)t * k + j];
+                if (e >= 0 && e < E) atomicOr(&masks[c * E + e], 1ull << lane);
+            }
+    }
+    __syncthreads();
+    // per expert: running in-group prefix and kept base over the chunks
+    int kept_total = 0;
+    if (tid < E) {
+        int run = 0;
+        for (int c = 0; c < nc; ++c) {
+            const int cnt = __popcll(masks[c * E + tid]);
+            if (group_chunks > 0 && c % group_chunks == 0) run = 0;
+            pre[c * E + tid] = run;
+            int kept = cnt;
+            if (capacity > 0) {
+                const int room = capacity - run;
+                kept = room <= 0 ? 0 : (room < cnt ? room : cnt);
+            }
+            base[c * E + tid] = kept_total;
+            kept_total += kept;
+            run += cnt;
+        }
+        counts[tid] = kept_total;
+    }
+    // exclusive scan of the kept counts over experts (thread order)
+    int incl = kept_total;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int n = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += n;
+    }
+    if (lane == kWave - 1) wsum[wave] = incl;
+    __syncthreads();
+    int before = 0, total = 0;
+    for (int w = 0; w < kSmallThreads / kWave; ++w) {
+        if (w < wave) before += wsum[w];
+        total += wsum[w];
+    }
+    if (tid < E) {
+        offs[tid] = before + incl - kept_total;
+        offsets[tid] = before + incl - kept_total;
+    }
+    if (tid == 0) offsets[E] = total;
+    __syncthreads();
+    // rows: offsets[e] + base + rank inside the chunk, or -1 past the capacity
+    const int64_t n = (int64_t)T * k;
+    for (int64_t i = tid; i < n; i += kSmallThreads) {
+        const int t = (int)(i / k);
+        const int e = idx[i];
+        if (e < 0 || e >= E) {
+            slot_row[i] = -1;
+            continue;
+        }
+        const int ce = (t / kChunk) * E + e;
+        const int r = __popcll(masks[ce] & ((1ull << (t % kChunk)) - 1ull));
+        if (capacity > 0 && pre[ce] + r >= capacity) {
+            slot_row[i] = -1;
+            continue;
+        }
+        const int row = offs[e] + base[ce] + r;
+        slot_row[i] = row;
+        row_token[row] = t;
+    }
+}
+
+bool permute_small_fits(int T, int E, int k) {
+    const int64_t nc = ((int64_t)T + kChunk - 1) / kChunk;
+    return E <= kMaxSmallExperts && nc * E * 16 <= kSmallLdsBytes && (int64_t)T * k <= kSmallMaxSlots;
+}
+
+void launch_permute_small(const PermuteArgs &a, hipStream_t s) {
+    const int64_t nc = ((int64_t)a.T + kChunk - 1) / kChunk;
+    hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(kSmallThreads), (size_t)(nc * a.E * 16), s, a.idx, a.T,
+                       a.E, a.k, a.capacity, a.group_chunks, a.counts, a.offsets, a.row_token, a.slot_row);
+}
+
 void launch_permute_count(const PermuteArgs &a, hipStream_t s) {
     const int64_t nc = ((int64_t)a.T + kChunk - 1) / kChunk;
     const size_t shmem = (size_t)4 * a.E * sizeof(unsigned long long);

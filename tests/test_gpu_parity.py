@@ -102,7 +102,15 @@ def test_fused_route_bit_exact_on_exact_inputs(spec):
 
 PERM_CASES = [  # T, E, k, capacity_factor, group
     (777, 8, 2, 0.0, 0), (4096, 16, 1, 1.25, 1024), (8192, 256, 8, 0.0, 0), (640, 16, 1, 1.25, 320),
-    (1000, 16, 1, 1.25, 0), (130, 64, 6, 0.0, 0), (64, 1, 1, 0.0, 0), (1, 4, 4, 0.0, 0)]
+    (1000, 16, 1, 1.25, 0), (130, 64, 6, 0.0, 0), (64, 1, 1, 0.0, 0), (1, 4, 4, 0.0, 0),
+    # at and past the limits of the one-workgroup path (T*k <= 16384, chunk tables <= 48 KiB)
+    (16384, 8, 1, 0.0, 0), (1536, 128, 2, 0.0, 0), (1600, 128, 2, 0.0, 0), (20000, 16, 1, 1.25, 1024),
+    (3000, 64, 6, 0.0, 0)]
+
+
+def _small_path(T, E, k):
+    nc = (T + 63) // 64
+    return T * k <= 16384 and nc * E * 16 <= 48 * 1024
 
 
 @pytest.mark.parametrize("T,E,k,cf,group", PERM_CASES)
@@ -117,8 +125,15 @@ def test_permute_bit_exact(T, E, k, cf, group):
     r["topk_idx"].copy_(idx.reshape(-1).to(DEV))
     x_perm = torch.full((T * k, spec.d), -7.0, dtype=torch.bfloat16, device=DEV)
     ws = moe.alloc_workspace(cfg, moe.STAGE_PERMUTE, DEV)
+    moe.moe_timing_reset()
+    moe.moe_timing_enable(True)
     moe.moe_permute(cfg, x.to(DEV), moe.make_routing(r), x_perm, ws)
     torch.cuda.synchronize()
+    names = moe.moe_kernel_names()
+    launched = {n for i, n in enumerate(names) if moe.moe_timing_read(i)[1]}
+    moe.moe_timing_enable(False)
+    assert ("permute_small" in launched) == _small_path(T, E, k)
+    assert ("permute_count" in launched) != _small_path(T, E, k)
     cap = oracle.capacity(cf, group if group else T, E) if cf > 0 else 0
     ref = oracle.permute(idx.numpy(), E, cap, group)
     n = ref["kept"]
