@@ -711,7 +711,7 @@ void launch_grouped_gemm(const GemmArgs &a, int shape, hipStream_t s) {
     // Tile shapes measured on the Mixtral-shape prefill GEMMs (T=4096, k=2,
     // d=4096, F=14336): 8 waves (2 per SIMD) with 256-row tiles, two K tiles
     // in flight, fragments double-buffered, on 16x16x32 MFMAs.  The 128- and
-    // 32-row tiles stay on 32x32x16, which measured faster there.
+    // 32-row tiles stay on 32x32x16, which measured faster for them.
     // Alternating single launches of two variants (so both see the same
     // power and clock state) measured: 16x16x32 MFMAs 2.5% faster than
     // 32x32x16 on both GEMMs; row halves split across the two waves of a
@@ -727,8 +727,12 @@ void launch_grouped_gemm(const GemmArgs &a, int shape, hipStream_t s) {
         if (glu) launch_bf16_t<32, 128, 1, 4, true, true, 2, false, 32>(a, s);
         else launch_bf16_t<32, 128, 1, 4, false, true, 2, false, 32>(a, s);
     } else if (shape == kGemmSmallM) {
-        if (glu) launch_bf16_t<128, 128, 2, 2, true, true, 2, true, 32>(a, s);
-        else launch_bf16_t<128, 256, 2, 2, false, true, 2, true, 32>(a, s);
+        // 8 waves (2 per SIMD) rather than 4: on the expert-choice layer
+        // (128 rows per expert) the down projection 112 -> 90 us, gate/up
+        // 171 -> 165 us; on the Switch layer 41 -> 28 and 50 -> 38 us.
+        // Splitting these short tiles along K measured 2x slower.
+        if (glu) launch_bf16_t<128, 128, 2, 4, true, true, 2, false, 32>(a, s);
+        else launch_bf16_t<128, 256, 2, 4, false, true, 2, false, 32>(a, s);
     } else {
         if (a.ragged) {
             if (glu) launch_bf16_t<256, 128, 2, 4, true, true, 2, false, 16, false, true, 0>(a, s);
