@@ -67,8 +67,10 @@ void launch_gather_rows(const void *x, const int32_t *row_token, const int32_t *
 // {mstart[g], g, offsets[g], offsets[g+1]} of its expert g.  Also clears the split-K arrival counters cnt[0 .. ncnt) (cnt may
 // be null).  E <= kMaxPlanExperts.
 constexpr int kMaxPlanExperts = 1024;
+// interleave: light experts (fewer rows than BM) spread evenly among the
+// heavy experts' m-tiles instead of expert order (see tile_plan_kernel).
 void launch_tile_plan(const int32_t *counts, const int32_t *offsets, int E, int BM, int32_t *mstart, int4 *mtile,
-                      int max_mt, int32_t *cnt, int ncnt, hipStream_t s);
+                      int max_mt, int32_t *cnt, int ncnt, bool interleave, hipStream_t s);
 // capacity of the m-tile table for rows routed rows over E experts (any BM >= 32)
 inline int64_t max_mtiles(int64_t rows, int E) { return (rows + 31) / 32 + E; }
 
