@@ -81,3 +81,29 @@ def test_full_size_sampled_tokens(spec):
     err = rel_err(_np(y)[toks][ok], ref["y64"][ok])
     print(f"{spec.name}: sampled {ok.sum()} tokens, max rel err {err:.3e}, flips excluded {(~ok).sum()}")
     assert err <= TOL[spec.dtype]
+
+
+def test_forward_with_x_of_two_gib():
+    """x of exactly 2 GiB (T = 131072, d = 8192): one 32-bit buffer offset no
+    longer spans it, so the forward pass gathers the routed rows with the
+    gather kernel before the first GEMM instead of inside it; 64-bit row
+    offsets throughout.  Sampled tokens against the oracle."""
+    spec = workloads.MIXTRAL_PREFILL_BF16.replace(name="x_two_gib", T=131072, d=8192, E=4, k=1, F=64)
+    assert spec.T * spec.d * 2 == 1 << 31
+    inp = workloads.make_inputs(spec, device=DEV)
+    y, routing = run_forward(spec, inp)
+    counts = _np(routing["counts"])
+    assert counts.sum() == spec.T and (counts > 0).all()
+    toks = _sample(spec.T, 12)
+    ref = oracle.forward_tokens(spec, inp, toks)
+    flips, near, _ = token_choice_flips(_np(routing["topk_idx"]).reshape(spec.T, 1)[toks], ref["topk_idx"],
+                                        _np(routing["logits"]).reshape(spec.T, spec.E)[toks], ref["logits_sel"], 1)
+    assert near.all()
+    ok = np.ones(len(toks), bool)
+    ok[flips] = False
+    ys = _np(y[torch.from_numpy(toks).to(DEV)])
+    err = rel_err(ys[ok], ref["y64"][ok])
+    print(f"x_two_gib: sampled {ok.sum()} tokens, max rel err {err:.3e}")
+    assert err <= TOL[spec.dtype]
+    del inp, y, routing
+    torch.cuda.empty_cache()
