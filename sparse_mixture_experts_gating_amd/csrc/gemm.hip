@@ -512,67 +512,108 @@ struct GemmParamsF32 {
     int act;
 };
 
-constexpr int kF32BM = 64;
+constexpr int kF32BM = 32;
 
+// Float32 grouped GEMM on the vector ALU: 32x32 tiles (small tiles, so that
+// the few rows of a float32 layer still spread over many CUs), K steps of
+// 64, each of the 256 threads 2x2 outputs (2x2 more for the up projection).
+// The next K step's operands are loaded into registers (16-byte loads)
+// while the current one is computed from LDS.  Rows past the group's end and
+// columns past N read a valid row (results discarded); K positions past K
+// read zeros.
 template <bool GLU>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParamsF32 p) {
-    constexpr int BM = kF32BM, BN = 64, BK = 16;
-    __shared__ float As[BK][BM + 4];
-    __shared__ float Bs[BK][BN + 4];
-    __shared__ float Bu[GLU ? BK : 1][BN + 4];
+    constexpr int BM = kF32BM, BN = 32, BK = 64;
+    constexpr int NU = GLU ? 2 : 1;
+    __shared__ float As[BK][BM + 1];
+    __shared__ float Bs[NU][BK][BN + 1];
     const int ntn = (p.N + BN - 1) / BN;
     const TileCoord tc = find_tile<BM>(xcd_remap(blockIdx.x), p.offsets, p.mstart, p.mtile, p.max_mt, p.G, p.rows, ntn);
     if (!tc.valid) return;
     const int n0 = tc.nt * BN;
     const int64_t K = p.K;
-    const float *B0g = p.B0 + (int64_t)tc.g * p.N * K;
-    const float *B1g = GLU ? p.B1 + (int64_t)tc.g * p.N * K : nullptr;
+    const float *Bg[NU];
+    Bg[0] = p.B0 + (int64_t)tc.g * p.N * K;
+    if constexpr (GLU) Bg[NU - 1] = p.B1 + (int64_t)tc.g * p.N * K;
     const int tid = threadIdx.x, tx = tid % 16, ty = tid / 16;
-    float acc[4][4] = {}, accu[GLU ? 4 : 1][GLU ? 4 : 1] = {};
-    // loader: element (r, kk) with r = q / 16, kk = q % 16 for q = tid + 256 * i
-    for (int k0 = 0; k0 < p.K; k0 += BK) {
+    float acc[NU][2][2] = {};
+    // loader: float4 q = tid + 256 * i holds k = 4 * (q % 16) .. +3 of tile row q / 16
+    const float *arow[2], *brow[NU][2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int q = tid + 256 * i, r = q / BK, kk = q % BK;
-            int64_t gr = tc.row0 + r;
-            if (gr >= tc.row_end) gr = tc.row_end - 1;
-            As[kk][r] = p.A[gr * K + k0 + kk];
-            int n = n0 + r;
-            if (n >= p.N) n = p.N - 1;
-            Bs[kk][r] = B0g[(int64_t)n * K + k0 + kk];
-            if constexpr (GLU) Bu[kk][r] = B1g[(int64_t)n * K + k0 + kk];
+    for (int i = 0; i < 2; ++i) {
+        const int r = (tid + 256 * i) / 16;
+        int64_t gr = tc.row0 + r;
+        if (gr >= tc.row_end) gr = tc.row_end - 1;
+        arow[i] = p.A + gr * K;
+        int n = n0 + r;
+        if (n >= p.N) n = p.N - 1;
+#pragma unroll
+        for (int u = 0; u < NU; ++u) brow[u][i] = Bg[u] + (int64_t)n * K;
+    }
+    const int kq = 4 * (tid % 16);
+    float4 ra[2], rb[NU][2];
+    auto gload = [&](int k0) {
+        const int k = k0 + kq;
+        const bool in = k < p.K;  // K is a multiple of 16: a float4 is all in or all out
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            ra[i] = in ? *(const float4 *)(arow[i] + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int u = 0; u < NU; ++u)
+                rb[u][i] = in ? *(const float4 *)(brow[u][i] + k) : make_float4(0.f, 0.f, 0.f, 0.f);
         }
+    };
+    auto lstore = [&]() {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int r = (tid + 256 * i) / 16;
+            As[kq][r] = ra[i].x;
+            As[kq + 1][r] = ra[i].y;
+            As[kq + 2][r] = ra[i].z;
+            As[kq + 3][r] = ra[i].w;
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+                Bs[u][kq][r] = rb[u][i].x;
+                Bs[u][kq + 1][r] = rb[u][i].y;
+                Bs[u][kq + 2][r] = rb[u][i].z;
+                Bs[u][kq + 3][r] = rb[u][i].w;
+            }
+        }
+    };
+    gload(0);
+    for (int k0 = 0; k0 < p.K; k0 += BK) {
+        lstore();
         __syncthreads();
-#pragma unroll
+        if (k0 + BK < p.K) gload(k0 + BK);
+#pragma unroll 16
         for (int kk = 0; kk < BK; ++kk) {
-            float a[4], b[4], bu[4];
+            float a[2], b[NU][2];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                a[i] = As[kk][ty * 4 + i];
-                b[i] = Bs[kk][tx * 4 + i];
-                if constexpr (GLU) bu[i] = Bu[kk][tx * 4 + i];
+            for (int i = 0; i < 2; ++i) {
+                a[i] = As[kk][ty * 2 + i];
+#pragma unroll
+                for (int u = 0; u < NU; ++u) b[u][i] = Bs[u][kk][tx * 2 + i];
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int u = 0; u < NU; ++u)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
-                    if constexpr (GLU) accu[i][j] = fmaf(a[i], bu[j], accu[i][j]);
-                }
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) acc[u][i][j] = fmaf(a[i], b[u][j], acc[u][i][j]);
         }
         __syncthreads();
     }
     const float *bias = p.bias ? p.bias + (int64_t)tc.g * p.N : nullptr;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int64_t row = tc.row0 + ty * 4 + i;
+    for (int i = 0; i < 2; ++i) {
+        const int64_t row = tc.row0 + ty * 2 + i;
         if (row >= tc.row_end) continue;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int col = n0 + tx * 4 + j;
+        for (int j = 0; j < 2; ++j) {
+            const int col = n0 + tx * 2 + j;
             if (col >= p.N) continue;
-            float v = acc[i][j];
-            if constexpr (GLU) v = silu(v) * accu[i][j];
+            float v = acc[0][i][j];
+            if constexpr (GLU) v = silu(v) * acc[NU - 1][i][j];
             else v = apply_act(p.act, v + (bias ? bias[col] : 0.f));
             p.C[row * p.N + col] = v;
         }
@@ -757,7 +798,7 @@ template <bool GLU>
 static void launch_f32_t(const GemmArgs &a, hipStream_t s) {
     GemmParamsF32 p{(const float *)a.A, (const float *)a.B0, (const float *)a.B1, a.bias, (float *)a.C,
                     a.offsets, a.mstart, a.mtile, a.max_mt, a.G, a.rows, a.N, a.K, a.act};
-    const int64_t grid = grid_for(a, kF32BM, 64);
+    const int64_t grid = grid_for(a, kF32BM, 32);
     if (grid == 0) return;
     hipLaunchKernelGGL((gemm_f32_kernel<GLU>), dim3((unsigned)grid), dim3(256), 0, s, p);
 }
