@@ -177,25 +177,57 @@ __global__ __launch_bounds__(kSmallThreads) void permute_small_kernel(const int3
             }
     }
     __syncthreads();
-    // per expert: running in-group prefix and kept base over the chunks
-    int kept_total = 0;
-    if (tid < E) {
-        int run = 0;
-        for (int c = 0; c < nc; ++c) {
-            const int cnt = __popcll(masks[c * E + tid]);
-            if (group_chunks > 0 && c % group_chunks == 0) run = 0;
-            pre[c * E + tid] = run;
-            int kept = cnt;
-            if (capacity > 0) {
-                const int room = capacity - run;
-                kept = room <= 0 ? 0 : (room < cnt ? room : cnt);
-            }
-            base[c * E + tid] = kept_total;
-            kept_total += kept;
-            run += cnt;
+    // per expert, one wave: wave-wide scans over windows of 64 chunks give
+    //   P(c)   = assignments to e in chunks 0..c                (into base)
+    //   pre(c) = P(c) - cnt(c) - P(first chunk of c's group - 1)  (into pre)
+    //   base(c) = kept assignments to e in chunks before c      (into base)
+    __shared__ int ktot[kMaxSmallExperts];
+    auto wave_incl = [&](int v) {
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const int n = __shfl_up(v, o, kWave);
+            if (lane >= o) v += n;
         }
-        counts[tid] = kept_total;
+        return v;
+    };
+    for (int e = wave; e < E; e += kSmallThreads / kWave) {
+        int carry = 0;
+        for (int c0 = 0; c0 < nc; c0 += kWave) {
+            const int c = c0 + lane;
+            const int incl = wave_incl(c < nc ? __popcll(masks[c * E + e]) : 0);
+            if (c < nc) base[c * E + e] = carry + incl;
+            carry += __shfl(incl, kWave - 1, kWave);
+        }
+        for (int c0 = 0; c0 < nc; c0 += kWave) {
+            const int c = c0 + lane;
+            if (c < nc) {
+                const int head = group_chunks > 0 ? c - c % group_chunks : 0;
+                pre[c * E + e] = base[c * E + e] - __popcll(masks[c * E + e]) - (head > 0 ? base[(head - 1) * E + e] : 0);
+            }
+        }
+        carry = 0;
+        for (int c0 = 0; c0 < nc; c0 += kWave) {
+            const int c = c0 + lane;
+            int kept = 0;
+            if (c < nc) {
+                const int cnt = __popcll(masks[c * E + e]);
+                kept = cnt;
+                if (capacity > 0) {
+                    const int room = capacity - pre[c * E + e];
+                    kept = room <= 0 ? 0 : (room < cnt ? room : cnt);
+                }
+            }
+            const int incl = wave_incl(kept);
+            if (c < nc) base[c * E + e] = carry + incl - kept;
+            carry += __shfl(incl, kWave - 1, kWave);
+        }
+        if (lane == 0) {
+            ktot[e] = carry;
+            counts[e] = carry;
+        }
     }
+    __syncthreads();
+    const int kept_total = tid < E ? ktot[tid] : 0;
     // exclusive scan of the kept counts over experts (thread order)
     int incl = kept_total;
 #pragma unroll
