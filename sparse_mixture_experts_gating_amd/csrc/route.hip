@@ -498,6 +498,36 @@ __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(const float *__re
     }
     int P = 1;
     while (P < C) P <<= 1;
+    if (P <= 2 * kWave) {
+        // Up to 128 candidates: wave 0 sorts them in registers, two per lane
+        // (elements lane and lane + 64), with a bitonic network of register
+        // compares and lane exchanges; zero keys pad to 128 and sort last.
+        __syncthreads();
+        if (wave == 0) {
+            const int lane = tid;
+            uint64_t v0 = lane < C ? cand[lane] : 0ull, v1 = lane + kWave < C ? cand[lane + kWave] : 0ull;
+            for (int size = 2; size <= 2 * kWave; size <<= 1) {
+                for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                    if (stride == kWave) {  // partners in one lane: element lane (lower) and lane + 64
+                        const bool desc = (lane & size) == 0;
+                        const uint64_t hi = v0 > v1 ? v0 : v1, lo = v0 > v1 ? v1 : v0;
+                        v0 = desc ? hi : lo;
+                        v1 = desc ? lo : hi;
+                    } else {
+                        const uint64_t p0 = shfl_xor_u64(v0, stride), p1 = shfl_xor_u64(v1, stride);
+                        const bool lower = (lane & stride) == 0;
+                        const bool d0 = (lane & size) == 0, d1 = ((lane + kWave) & size) == 0;
+                        // the lower index keeps the larger key when descending
+                        v0 = (lower == d0) ? (v0 > p0 ? v0 : p0) : (v0 < p0 ? v0 : p0);
+                        v1 = (lower == d1) ? (v1 > p1 ? v1 : p1) : (v1 < p1 ? v1 : p1);
+                    }
+                }
+            }
+            cand[lane] = v0;
+            cand[lane + kWave] = v1;
+        }
+        __syncthreads();
+    } else {
     for (int i = C + tid; i < P; i += kEcThreads) cand[i] = 0ull;
     __syncthreads();
     for (int size = 2; size <= P; size <<= 1) {
@@ -514,6 +544,7 @@ __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(const float *__re
             }
             __syncthreads();
         }
+    }
     }
     for (int j = tid; j < C; j += kEcThreads) {
         const uint64_t kk = cand[j];
