@@ -19,6 +19,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "plan.h"
 
 namespace moe {
 
@@ -623,102 +624,13 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParamsF32 p) {
 // ---------------------------------------------------------------------------
 // tile plan
 // ---------------------------------------------------------------------------
-// Number of light experts placed before heavy m-tile h when nl light experts
-// are spread over Mh heavy m-tiles: light j goes after q_j = floor((2j+1) Mh
-// / (2 nl)) heavy m-tiles, and q_j <= h  <=>  2j+1 < 2 nl (h+1) / Mh.
-__device__ inline int lights_before(int64_t h, int64_t Mh, int64_t nl) {
-    if (nl == 0) return 0;
-    if (Mh == 0) return (int)nl;
-    const int64_t c = (2 * nl * (h + 1) + Mh - 1) / Mh;
-    return (int)(c / 2 < nl ? c / 2 : nl);
-}
-
 __global__ __launch_bounds__(256) void tile_plan_kernel(const int32_t *__restrict__ counts,
                                                         const int32_t *__restrict__ offsets, int E, int BM,
                                                         int32_t *__restrict__ mstart, int4 *__restrict__ mtile,
                                                         int max_mt, int32_t *__restrict__ cnt, int ncnt,
                                                         int interleave) {
-    __shared__ int ms[kMaxPlanExperts + 1];  // first m-tile of each expert (expert order)
-    __shared__ int hs[kMaxPlanExperts + 1];  // heavy m-tiles before each expert
-    __shared__ int ls[kMaxPlanExperts + 1];  // light experts before each expert
-    const int tid = threadIdx.x, lane = tid % kWave;
-    for (int i = tid; i < ncnt; i += 256) cnt[i] = 0;
-    if (tid < kWave) {
-        int base = 0, hbase = 0, lbase = 0;
-        for (int e0 = 0; e0 < E; e0 += kWave) {
-            const int e = e0 + lane;
-            const int c = e < E ? counts[e] : 0;
-            const int v = (c + BM - 1) / BM;
-            const int hv = c >= BM ? v : 0, lv = c > 0 && c < BM ? 1 : 0;
-            int incl = v, hincl = hv, lincl = lv;
-#pragma unroll
-            for (int o = 1; o < kWave; o <<= 1) {
-                const int n = __shfl_up(incl, o, kWave), hn = __shfl_up(hincl, o, kWave);
-                const int ln = __shfl_up(lincl, o, kWave);
-                if (lane >= o) {
-                    incl += n;
-                    hincl += hn;
-                    lincl += ln;
-                }
-            }
-            if (e < E) {
-                mstart[e] = base + incl - v;
-                ms[e] = base + incl - v;
-                hs[e] = hbase + hincl - hv;
-                ls[e] = lbase + lincl - lv;
-            }
-            base += __shfl(incl, kWave - 1, kWave);
-            hbase += __shfl(hincl, kWave - 1, kWave);
-            lbase += __shfl(lincl, kWave - 1, kWave);
-        }
-        if (lane == 0) {
-            mstart[E] = base;
-            ms[E] = base;
-            hs[E] = hbase;
-            ls[E] = lbase;
-        }
-    }
-    __syncthreads();
-    if (!interleave) {
-        for (int e = tid; e < E; e += 256) {
-            const int first = ms[e], n = ms[e + 1] - first;
-            const int4 info = make_int4(first, e, offsets[e], offsets[e + 1]);
-            for (int m = 0; m < n && first + m < max_mt; ++m) mtile[first + m] = info;
-        }
-        return;
-    }
-    // Interleaved order: the light experts (fewer rows than one tile: their
-    // tiles stream weights for a few rows) are spread evenly among the
-    // m-tiles of the heavy experts (whose tiles are MFMA-bound), so that
-    // every round of tiles mixes both kinds.  A heavy expert's m-tiles stay
-    // in order; a light expert between two of them splits it into runs, and
-    // each run is one table group (its own first m-tile and row range).
-    const int64_t Mh = hs[E], nl = ls[E];
-    for (int e = tid; e < E; e += 256) {
-        const int c = offsets[e + 1] - offsets[e];
-        if (c <= 0) continue;
-        if (c < BM) {
-            const int64_t j = ls[e];
-            const int64_t pos = (2 * j + 1) * Mh / (2 * nl) + j;
-            if (pos < max_mt) mtile[pos] = make_int4((int)pos, e, offsets[e], offsets[e + 1]);
-            continue;
-        }
-        const int n = ms[e + 1] - ms[e];
-        int m0 = 0;
-        for (int m = 0; m < n; ++m) {
-            const int64_t h = hs[e] + m;
-            const bool last = m + 1 == n || lights_before(h + 1, Mh, nl) != lights_before(h, Mh, nl);
-            if (!last) continue;
-            // run m0 .. m: consecutive table positions from that of m-tile m0
-            const int64_t h0 = hs[e] + m0;
-            const int64_t x = h0 + lights_before(h0, Mh, nl);
-            const int z = offsets[e] + m0 * BM;
-            const int w = min(offsets[e + 1], offsets[e] + (m + 1) * BM);
-            for (int q = m0; q <= m; ++q)
-                if (x + q - m0 < max_mt) mtile[x + q - m0] = make_int4((int)x, e, z, w);
-            m0 = m + 1;
-        }
-    }
+    __shared__ int scratch[3 * (kMaxPlanExperts + 1)];
+    build_tile_plan(counts, offsets, E, BM, mstart, mtile, max_mt, cnt, ncnt, interleave != 0, scratch);
 }
 
 void launch_tile_plan(const int32_t *counts, const int32_t *offsets, int E, int BM, int32_t *mstart, int4 *mtile,

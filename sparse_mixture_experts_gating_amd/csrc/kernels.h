@@ -48,10 +48,21 @@ struct PermuteArgs {
 // chunk tables fit: E <= kMaxSmallExperts, nc * E * 16 <= kSmallLdsBytes and
 // T * k <= kSmallMaxSlots.  Writes counts, offsets, row_token and slot_row.
 constexpr int kMaxSmallExperts = 1024;
-constexpr int kSmallLdsBytes = 48 * 1024;
+constexpr int kSmallLdsBytes = 40 * 1024;
 constexpr int kSmallMaxSlots = 16384;
 bool permute_small_fits(int T, int E, int k);
-void launch_permute_small(const PermuteArgs &a, hipStream_t s);
+// The grouped GEMMs' tile plan (see launch_tile_plan), built at the end of
+// the one-workgroup permutation when mstart is not null.
+struct TilePlanArgs {
+    int BM;
+    int32_t *mstart;
+    int4 *mtile;
+    int max_mt;
+    int32_t *cnt;
+    int ncnt;
+    bool interleave;
+};
+void launch_permute_small(const PermuteArgs &a, const TilePlanArgs &plan, hipStream_t s);
 void launch_permute_count(const PermuteArgs &a, hipStream_t s);
 void launch_permute_scan(const PermuteArgs &a, hipStream_t s);
 void launch_permute_scatter(const PermuteArgs &a, hipStream_t s);

@@ -308,8 +308,11 @@ moe_status do_route(const Derived &D, const void *x, const moe_weights *w, const
     return MOE_OK;
 }
 
+// plan non-null: when the one-workgroup permutation runs, it also builds the
+// grouped GEMMs' tile plan and *plan_built is set.
 moe_status do_permute(const Derived &D, const void *x, const moe_routing *r, void *x_perm, char *ws,
-                      const PermuteWs &pw, hipStream_t s, bool gather = true) {
+                      const PermuteWs &pw, hipStream_t s, bool gather = true, const TilePlanArgs *plan = nullptr,
+                      bool *plan_built = nullptr) {
     if (D.T == 0) return MOE_OK;
     if (D.ec) {
         TRY(launch(K_EC_PERMUTE, s, [&] {
@@ -321,7 +324,9 @@ moe_status do_permute(const Derived &D, const void *x, const moe_routing *r, voi
                       (int32_t *)(ws + pw.counts), (int32_t *)(ws + pw.pre), (int32_t *)(ws + pw.base),
                       (int32_t *)(ws + pw.ranks), r->counts, r->offsets, r->row_token, r->slot_row};
         if (permute_small_fits((int)D.T, (int)D.E, (int)D.k)) {
-            TRY(launch(K_PERM_SMALL, s, [&] { launch_permute_small(a, s); }));
+            const TilePlanArgs none{0, nullptr, nullptr, 0, nullptr, 0, false};
+            TRY(launch(K_PERM_SMALL, s, [&] { launch_permute_small(a, plan ? *plan : none, s); }));
+            if (plan && plan_built) *plan_built = true;
         } else {
             TRY(launch(K_PERM_COUNT, s, [&] { launch_permute_count(a, s); }));
             TRY(launch(K_PERM_SCAN, s, [&] { launch_permute_scan(a, s); }));
@@ -353,26 +358,37 @@ int pick_shape(const Derived &D) {
     return kGemmPrefill;
 }
 
+// average rows per expert under four 256-row tiles: most tiles are ragged
+bool ragged_layer(const Derived &D) { return D.a_max < 4 * 256 * D.E; }
+
+// Tile plan of the grouped GEMMs for this layer, in the FFN workspace.
+// Ragged layers spread the tiles of experts with less than a tile of rows
+// among the others (DeepSeek-style layer: down projection -2.5%).
+TilePlanArgs plan_args(const Derived &D, char *ws, const FfnWs &fw) {
+    return TilePlanArgs{gemm_block_m(pick_shape(D), D.bf16), (int32_t *)(ws + fw.mstart), (int4 *)(ws + fw.mtile),
+                        fw.max_mt, D.bf16 ? (int32_t *)(ws + fw.cnt) : nullptr, D.bf16 ? fw.ncnt : 0,
+                        ragged_layer(D)};
+}
+
 // x_perm null: the first GEMM reads the routed rows straight from x through
 // the row map (bf16, x within one buffer resource; see gather_in_gemm).
+// plan_built: the permutation already wrote the tile plan (plan_args).
 moe_status do_ffn(const Derived &D, const void *x_perm, const void *x, const moe_routing *r, const moe_weights *w,
-                  void *y_perm, void *y_shared, char *ws, const FfnWs &fw, hipStream_t s) {
+                  void *y_perm, void *y_shared, char *ws, const FfnWs &fw, hipStream_t s, bool plan_built = false) {
     if (D.T == 0) return MOE_OK;
     const int shape = pick_shape(D);
-    const int BM = gemm_block_m(shape, D.bf16);
-    int32_t *mstart = (int32_t *)(ws + fw.mstart);
+    const TilePlanArgs plan = plan_args(D, ws, fw);
+    int32_t *mstart = plan.mstart;
+    int4 *mtile = plan.mtile;
     void *H = ws + fw.h;
     const SplitKWs split{D.bf16 ? (float *)(ws + fw.part) : nullptr, fw.part_floats,
                          D.bf16 ? (int32_t *)(ws + fw.cnt) : nullptr, fw.ncnt};
-    int4 *mtile = (int4 *)(ws + fw.mtile);
-    // average rows per expert under four 256-row tiles: most tiles are ragged
-    const bool ragged = D.a_max < 4 * 256 * D.E;
-    // ragged layers spread the tiles of experts with less than a tile of rows
-    // among the others (DeepSeek-style layer: down projection -2.5%)
-    TRY(launch(K_TILE_PLAN, s, [&] {
-        launch_tile_plan(r->counts, r->offsets, (int)D.E, BM, mstart, mtile, fw.max_mt, split.cnt, split.ncnt,
-                         ragged, s);
-    }));
+    const bool ragged = plan.interleave;
+    if (!plan_built)
+        TRY(launch(K_TILE_PLAN, s, [&] {
+            launch_tile_plan(r->counts, r->offsets, (int)D.E, plan.BM, mstart, mtile, fw.max_mt, split.cnt,
+                             split.ncnt, plan.interleave, s);
+        }));
     GemmArgs g1{x_perm, w->w1, w->w3, w->b1, H, r->offsets, mstart, mtile, fw.max_mt, (int)D.E, D.a_max, (int)D.F,
                 (int)D.d, D.act == MOE_ACT_SWIGLU ? kActSwiglu : D.act, D.bf16, split, ragged};
     if (x_perm == nullptr) {
@@ -626,8 +642,10 @@ moe_status moe_forward(const moe_config *cfg, const void *x, const moe_weights *
     void *y_shared = D.Fs ? base + fw.y_shared : nullptr;
     TRY(do_route(D, x, w, &r, s));
     const bool fused = gather_in_gemm(D);
-    TRY(do_permute(D, x, &r, x_perm, base, fw.perm, s, !fused));
-    TRY(do_ffn(D, fused ? nullptr : x_perm, x, &r, w, y_perm, y_shared, base, fw.ffn, s));
+    const TilePlanArgs plan = plan_args(D, base, fw.ffn);
+    bool plan_built = false;
+    TRY(do_permute(D, x, &r, x_perm, base, fw.perm, s, !fused, &plan, &plan_built));
+    TRY(do_ffn(D, fused ? nullptr : x_perm, x, &r, w, y_perm, y_shared, base, fw.ffn, s, plan_built));
     return do_combine(D, y_perm, y_shared, &r, y, s);
 }
 

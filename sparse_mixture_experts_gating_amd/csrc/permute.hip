@@ -18,6 +18,7 @@
 //             prefix + rank >= C.
 #include "common.h"
 #include "kernels.h"
+#include "plan.h"
 
 namespace moe {
 
@@ -146,8 +147,9 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(const int32_t *__r
 // ---------------------------------------------------------------------------
 // Small batches: the three phases above in one workgroup, with the per-chunk
 // masks, prefixes and bases in LDS (nc * E * 16 bytes), so a decode-sized or
-// mid-sized batch pays one launch instead of three.  Same formulas, so the
-// same counts, offsets, rows and drops.
+// mid-sized batch pays one launch instead of three (four with the grouped
+// GEMMs' tile plan, which the forward pass builds here too).  Same formulas,
+// so the same counts, offsets, rows and drops.
 // ---------------------------------------------------------------------------
 constexpr int kSmallThreads = 1024;
 
@@ -156,7 +158,8 @@ __global__ __launch_bounds__(kSmallThreads) void permute_small_kernel(const int3
                                                                       int32_t *__restrict__ counts,
                                                                       int32_t *__restrict__ offsets,
                                                                       int32_t *__restrict__ row_token,
-                                                                      int32_t *__restrict__ slot_row) {
+                                                                      int32_t *__restrict__ slot_row,
+                                                                      TilePlanArgs plan) {
     extern __shared__ unsigned long long lds_u64[];
     const int nc = (T + kChunk - 1) / kChunk;
     unsigned long long *masks = lds_u64;                   // [nc][E]
@@ -246,7 +249,10 @@ __global__ __launch_bounds__(kSmallThreads) void permute_small_kernel(const int3
         offs[tid] = before + incl - kept_total;
         offsets[tid] = before + incl - kept_total;
     }
-    if (tid == 0) offsets[E] = total;
+    if (tid == 0) {
+        offsets[E] = total;
+        offs[E] = total;
+    }
     __syncthreads();
     // rows: offsets[e] + base + rank inside the chunk, or -1 past the capacity
     const int64_t n = (int64_t)T * k;
@@ -267,6 +273,11 @@ __global__ __launch_bounds__(kSmallThreads) void permute_small_kernel(const int3
         slot_row[i] = row;
         row_token[row] = t;
     }
+    if (plan.mstart != nullptr) {
+        __shared__ int plan_scratch[3 * (kMaxSmallExperts + 1)];
+        build_tile_plan(ktot, offs, E, plan.BM, plan.mstart, plan.mtile, plan.max_mt, plan.cnt, plan.ncnt,
+                        plan.interleave, plan_scratch);
+    }
 }
 
 bool permute_small_fits(int T, int E, int k) {
@@ -274,10 +285,10 @@ bool permute_small_fits(int T, int E, int k) {
     return E <= kMaxSmallExperts && nc * E * 16 <= kSmallLdsBytes && (int64_t)T * k <= kSmallMaxSlots;
 }
 
-void launch_permute_small(const PermuteArgs &a, hipStream_t s) {
+void launch_permute_small(const PermuteArgs &a, const TilePlanArgs &plan, hipStream_t s) {
     const int64_t nc = ((int64_t)a.T + kChunk - 1) / kChunk;
     hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(kSmallThreads), (size_t)(nc * a.E * 16), s, a.idx, a.T,
-                       a.E, a.k, a.capacity, a.group_chunks, a.counts, a.offsets, a.row_token, a.slot_row);
+                       a.E, a.k, a.capacity, a.group_chunks, a.counts, a.offsets, a.row_token, a.slot_row, plan);
 }
 
 void launch_permute_count(const PermuteArgs &a, hipStream_t s) {
