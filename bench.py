@@ -182,6 +182,31 @@ def main():
     tokens_per_s = spec.T / (ms / 1e3)
     layer_tflops = flops / (ms / 1e3) / 1e12
 
+    # the same step captured once in a HIP graph and replayed: what a caller
+    # that replays the layer pays without per-launch host overhead
+    graph_ms = None
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        for _ in range(max(args.warmup, 1)):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t0) * 1e3 / max(args.steps, 1)
+        del g
+    except RuntimeError as exc:  # capture not available: report the eager number only
+        log(f"[bench] graph capture skipped: {exc}")
+
     # per-kernel durations from HIP events recorded on the launch stream
     log("[bench] per-kernel event timing")
     moe.moe_timing_reset()
@@ -261,6 +286,7 @@ def main():
         "layer_tflops_active": round(layer_tflops, 2),
         "layer_frac_bf16_peak": round(layer_tflops / PEAK_BF16_TFLOPS, 4),
         "cold_ms_per_step": round(cold_ms, 4),
+        "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 4),
         "kernels_us": {n: v["avg_us"] for n, v in kern.items()},
         "kernels": kern,
         "roofline": roofline,
