@@ -560,42 +560,48 @@ __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(const float *__re
 // router, EP more columns hold the noise projection x.Wn).  Each K chunk of
 // 64 moves the x rows and the weight rows through registers into one of two
 // XOR-swizzled LDS buffers (rows past T or E read as zeros through the
-// buffer-load limit), and the 4 waves split the columns: wave w computes
-// TOK tokens x EPX/4 columns on v_mfma_f32_16x16x32_bf16.  The float32
+// buffer-load limit), and the NTH/64 waves split the columns: wave w computes
+// TOK tokens x EPX/(NTH/64) columns on v_mfma_f32_16x16x32_bf16.  The float32
 // logits then meet in LDS, the bias (and softplus(x.Wn) * noise) is added in
 // a fixed order, and each wave gates whole tokens.
 // ---------------------------------------------------------------------------
-template <int TOK, int EP, bool NOISY, int PD = 4>
-__global__ __launch_bounds__(256) void router_tile_kernel(
+template <int TOK, int EP, bool NOISY, int PD = 4, int NTH = 256>
+__global__ __launch_bounds__(NTH) void router_tile_kernel(
     const bf16 *__restrict__ x, const bf16 *__restrict__ wg, const float *__restrict__ bias, int T, int d, int E,
     int k, int gating, float *__restrict__ logits, int32_t *__restrict__ idx_out, float *__restrict__ w_out,
     const bf16 *__restrict__ wn, const float *__restrict__ noise) {
     constexpr int BK = 64;
+    constexpr int NW = NTH / kWave;           // waves
+    constexpr int RP = NTH / 8;               // rows one pass of 16-byte chunks covers
     constexpr int EPX = NOISY ? 2 * EP : EP;  // B rows: router weights, then the noise projection
     constexpr int ROWS = TOK + EPX;           // LDS rows per buffer
-    constexpr int WTN = EPX / 4;              // columns per wave
+    constexpr int WTN = EPX / NW;             // columns per wave
     constexpr int TM = TOK / 16, TN = WTN / 16;
-    constexpr int XPT = TOK / 32, WPT = EPX / 32;  // 16-byte chunks per thread and K chunk
-    static_assert(TM >= 1 && TN >= 1 && XPT >= 1 && WPT >= 1, "router tile");
+    // 16-byte chunks per thread and K chunk; with fewer x rows than one pass,
+    // the threads past them load duplicates and skip their LDS stores
+    constexpr int XPT = TOK >= RP ? TOK / RP : 1, WPT = EPX / RP;
+    static_assert(TM >= 1 && TN >= 1 && WPT >= 1 && (TOK % RP == 0 || RP % TOK == 0), "router tile");
     static_assert(2 * ROWS * BK * 2 >= TOK * EPX * 4, "the logits tile reuses the staging buffers");
     __shared__ __attribute__((aligned(16))) bf16 lds[2][ROWS * BK];
 
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int64_t tok0 = (int64_t)blockIdx.x * TOK;
-    const int r0 = tid / 8, ch0 = tid % 8;  // thread moves chunk ch0 of rows r0 + 32*i
+    const int r0 = tid / 8, ch0 = tid % 8;  // thread moves chunk ch0 of rows r0 + RP*i
+    const int xr0 = r0 % TOK;               // its x row (a duplicate when r0 >= TOK)
     const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(x + tok0 * d, (T - tok0) * (int64_t)d * 2);
     const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(wg, (int64_t)E * d * 2);
     const __amdgpu_buffer_rsrc_t nr = NOISY ? buffer_rsrc(wn, (int64_t)E * d * 2) : wr;
     uint32_t xoff[XPT], woff[WPT];
 #pragma unroll
-    for (int i = 0; i < XPT; ++i) xoff[i] = (uint32_t)(((int64_t)(r0 + 32 * i) * d + ch0 * 8) * 2);
+    for (int i = 0; i < XPT; ++i) xoff[i] = (uint32_t)(((int64_t)(xr0 + RP * i) * d + ch0 * 8) * 2);
 #pragma unroll
     for (int i = 0; i < WPT; ++i) {
-        const int r = r0 + 32 * i;
+        const int r = r0 + RP * i;
         woff[i] = (uint32_t)(((int64_t)(NOISY && r >= EP ? r - EP : r) * d + ch0 * 8) * 2);
     }
-    // rows r0 + 32*i (and TOK + r0 + 32*i, TOK a multiple of 16) share swz(r0)
+    // rows r0 + RP*i (and TOK + r0 + RP*i, TOK a multiple of 16) share swz(r0)
     const int sdst = r0 * BK + ((ch0 ^ swz(r0)) * 8);
+    const bool xstore = r0 < TOK;
     // PD register sets: chunk c is loaded into set c % PD, PD chunks ahead of
     // its MFMAs, so PD - 1 chunks stay in flight while one is computed.
     u32x4 rx[PD][XPT], rw[PD][WPT];
@@ -604,13 +610,15 @@ __global__ __launch_bounds__(256) void router_tile_kernel(
 #pragma unroll
         for (int i = 0; i < XPT; ++i) rx[set][i] = buffer_load16(xr, xoff[i], ko);
 #pragma unroll
-        for (int i = 0; i < WPT; ++i) rw[set][i] = buffer_load16(NOISY && 32 * i >= EP ? nr : wr, woff[i], ko);
+        for (int i = 0; i < WPT; ++i) rw[set][i] = buffer_load16(NOISY && RP * i >= EP ? nr : wr, woff[i], ko);
     };
     auto lstore = [&](bf16 *L, int set) {
+        if (xstore) {
 #pragma unroll
-        for (int i = 0; i < XPT; ++i) store16(L + sdst + i * 32 * BK, rx[set][i]);
+            for (int i = 0; i < XPT; ++i) store16(L + sdst + i * RP * BK, rx[set][i]);
+        }
 #pragma unroll
-        for (int i = 0; i < WPT; ++i) store16(L + TOK * BK + sdst + i * 32 * BK, rw[set][i]);
+        for (int i = 0; i < WPT; ++i) store16(L + TOK * BK + sdst + i * RP * BK, rw[set][i]);
     };
     f32x4 acc[TM][TN];
 #pragma unroll
@@ -668,7 +676,7 @@ __global__ __launch_bounds__(256) void router_tile_kernel(
             for (int q = 0; q < 4; ++q)
                 Lf[(i * 16 + 4 * (lane / 16) + q) * EPX + wave * WTN + j * 16 + lane % 16] = acc[i][j][q];
     __syncthreads();
-    for (int tt = wave; tt < TOK; tt += 4) {
+    for (int tt = wave; tt < TOK; tt += NW) {
         const int64_t t = tok0 + tt;
         if (t >= T) break;
         float *row = Lf + tt * EPX;
@@ -696,6 +704,10 @@ static void launch_router_tile_t(const RouteArgs &a, hipStream_t s) {
         hipLaunchKernelGGL((router_tile_kernel<TOK, EP, true, PDN>), dim3(grid), dim3(256), 0, s, (const bf16 *)a.x,
                            (const bf16 *)a.wg, a.bias, a.T, a.d, a.E, a.k, a.gating, a.logits, a.idx, a.w,
                            (const bf16 *)a.wn, a.noise);
+    else if constexpr (EP >= 128)  // 8 waves: 2 per SIMD (DeepSeek-style router 124 -> 109 us)
+        hipLaunchKernelGGL((router_tile_kernel<TOK, EP, false, 4, 512>), dim3(grid), dim3(512), 0, s,
+                           (const bf16 *)a.x, (const bf16 *)a.wg, a.bias, a.T, a.d, a.E, a.k, a.gating, a.logits,
+                           a.idx, a.w, nullptr, nullptr);
     else
         hipLaunchKernelGGL((router_tile_kernel<TOK, EP, false>), dim3(grid), dim3(256), 0, s, (const bf16 *)a.x,
                            (const bf16 *)a.wg, a.bias, a.T, a.d, a.E, a.k, a.gating, a.logits, a.idx, a.w,

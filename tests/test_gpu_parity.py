@@ -72,7 +72,15 @@ def test_expert_choice_select_bit_exact(T, E, ties):
 # fused router on exact (integer-valued) inputs
 # ---------------------------------------------------------------------------
 
-INT_SPECS = [s.replace(name=s.name + "_int", inputs="integer") for s in workloads.SMALL]
+INT_SPECS = [s.replace(name=s.name + "_int", inputs="integer") for s in workloads.SMALL] + [
+    # the LDS-staged router tiles with 128 and 256 expert columns, 32- and 64-token blocks
+    workloads.DEEPSEEK_SHARED_BF16.replace(name="router_e256_int", T=333, d=512, E=256, k=8, F=64, F_shared=0,
+                                           inputs="integer"),
+    workloads.DEEPSEEK_SHARED_BF16.replace(name="router_e128_int", T=300, d=1024, E=128, k=6, F=64, F_shared=0,
+                                           inputs="integer"),
+    workloads.DEEPSEEK_SHARED_BF16.replace(name="router_e256_t32768_int", T=32768, d=128, E=256, k=8, F=64,
+                                           F_shared=0, inputs="integer"),
+]
 
 
 @pytest.mark.parametrize("spec", INT_SPECS, ids=lambda s: s.name)
