@@ -95,7 +95,7 @@ def kernel_roofline(spec, flops, nbytes, seconds):
     return bound, nbytes / seconds / 1e9, PEAK_HBM_GBS, "GB/s"
 
 
-GEMM_SOURCES = ("gemm.hip", "common.h", "kernels.h")
+GEMM_SOURCES = ("gemm.hip", "plan.h", "common.h", "kernels.h")
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "hbm_traffic_mixtral_prefill.md")
 
 

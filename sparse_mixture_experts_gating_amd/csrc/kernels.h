@@ -79,7 +79,8 @@ void launch_gather_rows(const void *x, const int32_t *row_token, const int32_t *
 // be null).  E <= kMaxPlanExperts.
 constexpr int kMaxPlanExperts = 1024;
 // interleave: light experts (fewer rows than BM) spread evenly among the
-// heavy experts' m-tiles instead of expert order (see tile_plan_kernel).
+// heavy experts' m-tiles instead of expert order (build_tile_plan); only for
+// layers with fewer than 1024 routed rows per expert on average.
 void launch_tile_plan(const int32_t *counts, const int32_t *offsets, int E, int BM, int32_t *mstart, int4 *mtile,
                       int max_mt, int32_t *cnt, int ncnt, bool interleave, hipStream_t s);
 // capacity of the m-tile table for rows routed rows over E experts (any BM >= 32)

@@ -10,10 +10,13 @@ namespace moe {
 // Number of light experts placed before heavy m-tile h when nl light experts
 // are spread over Mh heavy m-tiles: light j goes after q_j = floor((2j+1) Mh
 // / (2 nl)) heavy m-tiles, and q_j <= h  <=>  2j+1 < 2 nl (h+1) / Mh.
-__device__ inline int lights_before(int64_t h, int64_t Mh, int64_t nl) {
+// 32-bit arithmetic: the interleaved plan is used for ragged layers only
+// (fewer than 1024 rows per expert on average, so Mh < 2^16 m-tiles), and nl
+// <= 1024 keeps 2 nl (h+1) and (2j+1) Mh below 2^28.
+__device__ inline int lights_before(uint32_t h, uint32_t Mh, uint32_t nl) {
     if (nl == 0) return 0;
     if (Mh == 0) return (int)nl;
-    const int64_t c = (2 * nl * (h + 1) + Mh - 1) / Mh;
+    const uint32_t c = (2 * nl * (h + 1) + Mh - 1) / Mh;
     return (int)(c / 2 < nl ? c / 2 : nl);
 }
 
@@ -80,30 +83,33 @@ __device__ inline void build_tile_plan(const int32_t *counts, const int32_t *off
     // every round of tiles mixes both kinds.  A heavy expert's m-tiles stay
     // in order; a light expert between two of them splits it into runs, and
     // each run is one table group (its own first m-tile and row range).
-    const int64_t Mh = hs[E], nl = ls[E];
+    const uint32_t Mh = hs[E], nl = ls[E];
     for (int e = tid; e < E; e += nthreads) {
         const int c = offsets[e + 1] - offsets[e];
         if (c <= 0) continue;
         if (c < BM) {
-            const int64_t j = ls[e];
-            const int64_t pos = (2 * j + 1) * Mh / (2 * nl) + j;
-            if (pos < max_mt) mtile[pos] = make_int4((int)pos, e, offsets[e], offsets[e + 1]);
+            const uint32_t j = ls[e];
+            const uint32_t pos = (2 * j + 1) * Mh / (2 * nl) + j;
+            if (pos < (uint32_t)max_mt) mtile[pos] = make_int4((int)pos, e, offsets[e], offsets[e + 1]);
             continue;
         }
         const int n = ms[e + 1] - ms[e];
+        const int off0 = offsets[e], off1 = offsets[e + 1];
+        // L is constant along a run, so x = h0 + L(h0) = h0 + L(h) for any h of it
+        uint32_t L = lights_before(hs[e], Mh, nl);
         int m0 = 0;
         for (int m = 0; m < n; ++m) {
-            const int64_t h = hs[e] + m;
-            const bool last = m + 1 == n || lights_before(h + 1, Mh, nl) != lights_before(h, Mh, nl);
-            if (!last) continue;
+            const uint32_t h = hs[e] + m;
+            const uint32_t Lnext = m + 1 < n ? lights_before(h + 1, Mh, nl) : L;
+            if (m + 1 < n && Lnext == L) continue;
             // run m0 .. m: consecutive table positions from that of m-tile m0
-            const int64_t h0 = hs[e] + m0;
-            const int64_t x = h0 + lights_before(h0, Mh, nl);
-            const int z = offsets[e] + m0 * BM;
-            const int w = min(offsets[e + 1], offsets[e] + (m + 1) * BM);
+            const int x = (int)(hs[e] + m0 + L);
+            const int z = off0 + m0 * BM;
+            const int w = min(off1, off0 + (m + 1) * BM);
             for (int q = m0; q <= m; ++q)
-                if (x + q - m0 < max_mt) mtile[x + q - m0] = make_int4((int)x, e, z, w);
+                if (x + q - m0 < max_mt) mtile[x + q - m0] = make_int4(x, e, z, w);
             m0 = m + 1;
+            L = Lnext;
         }
     }
 }
