@@ -114,7 +114,9 @@ struct GemmParams {
 // when the last round is partial (rem tiles), each of its tiles is split into
 // S = slots / rem parts along K, so that the last round is as wide as the
 // others and each part runs 1/S of the K loop.  The parts of a tile are
-// consecutive logical indices inside one run of 32, i.e. on one XCD.
+// consecutive logical indices, mostly inside one run of 32 (one XCD); their
+// partial sums meet through device-scope fences, so parts that straddle two
+// XCDs are as correct.
 struct WorkItem {
     int tile;    // logical tile
     int part;    // K part (0 when not split)
@@ -128,8 +130,9 @@ __device__ inline WorkItem work_item(int w, int ntiles, const GemmParams &p) {
     if (p.part == nullptr || ntiles <= 0) return it;
     const int rem = ntiles % p.slots;
     if (rem == 0) return it;
-    int S = min(p.slots / rem, p.max_split);
-    S = S > 1 ? 1 << (31 - __clz(S)) : 1;  // a power of two: the parts stay inside one 32-tile XCD run
+    // any part count (not only powers of two, which left the Mixtral-shape
+    // down projection's last round 62% full: 1043 -> 980 us)
+    const int S = min(p.slots / rem, p.max_split);
     if (S < 2) return it;
     const int full = ntiles - rem;
     if (w < full) return it;
