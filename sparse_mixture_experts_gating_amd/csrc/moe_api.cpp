@@ -348,13 +348,21 @@ bool gather_in_gemm(const Derived &D) { return D.bf16 && (int64_t)D.T * D.d * 2 
 int pick_shape(const Derived &D) {
     if (D.ec) return D.capacity <= 160 ? kGemmSmallM : kGemmPrefill;
     if (D.T <= 32) return kGemmDecode;
-    int64_t max_rows = D.T;
+    int64_t max_rows = D.T, kept_max = D.T * D.k;
     if (D.capacity > 0) {
         const int64_t groups = D.group_chunks ? (D.T + D.group_chunks * kChunk - 1) / (D.group_chunks * kChunk) : 1;
         max_rows = std::min<int64_t>(D.T, groups * D.capacity);
+        kept_max = std::min<int64_t>(kept_max, groups * D.capacity * D.E);
     }
     const double avg = (double)D.T * D.k / D.E;
-    if (avg <= 160.0 || max_rows <= 384) return kGemmSmallM;
+    if (avg <= 160.0 || max_rows <= 384) {
+        // When even the 128-row tiles of the down projection (N = d, 256
+        // columns a tile) cannot fill the CUs, each tile's K loop is the
+        // critical path; 32-row tiles spread the same work over more CUs
+        // (Switch layer: down projection 38 -> 18 us, gate/up 27 -> 22 us).
+        const int64_t tiles = ((kept_max + 127) / 128 + D.E) * ((D.d + 255) / 256);
+        return tiles < device_cus() ? kGemmDecode : kGemmSmallM;
+    }
     return kGemmPrefill;
 }
 

@@ -187,7 +187,7 @@ FFN_SPECS = workloads.SMALL + [workloads.MIXTRAL_DECODE_BF16.replace(name="mixtr
 # partials added by the last part); the other shapes run unsplit.
 LONG_K_SPECS = [
     workloads.MIXTRAL_PREFILL_BF16.replace(name="long_k_prefill_tiles", T=1000, d=2048, F=1024),
-    workloads.MIXTRAL_PREFILL_BF16.replace(name="long_k_small_m_tiles", T=300, d=2048, F=512),
+    workloads.MIXTRAL_PREFILL_BF16.replace(name="long_k_small_m_tiles", T=1200, d=4096, E=16, k=1, F=512),
     workloads.MIXTRAL_PREFILL_BF16.replace(name="long_k_decode_tiles", T=16, d=2048, F=2048),
 ]
 SPLITK_SPECS = [
