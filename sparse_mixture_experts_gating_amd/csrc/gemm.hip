@@ -102,8 +102,9 @@ struct GemmParams {
     // split K of the last, partial round of tiles (null part: off)
     float *part;      // [slots][BM * NB] float32 partial accumulators
     int32_t *cnt;     // [slots] arrival counters, zero between launches
-    int slots;        // workgroups resident at once (one per CU)
+    int slots;        // workgroups resident at once
     int max_split;    // at most this many K parts per tile
+    int max_slabs;    // partial tiles the part area holds
     // gathered A: row r of the grouped operand is row arow[r] of A, whose
     // a_bytes bytes one buffer resource covers (null: rows in place)
     const int32_t *arow;
@@ -130,9 +131,19 @@ __device__ inline WorkItem work_item(int w, int ntiles, const GemmParams &p) {
     if (p.part == nullptr || ntiles <= 0) return it;
     const int rem = ntiles % p.slots;
     if (rem == 0) return it;
-    // any part count (not only powers of two, which left the Mixtral-shape
-    // down projection's last round 62% full: 1043 -> 980 us)
-    const int S = min(p.slots / rem, p.max_split);
+    // The part count S minimises the split tiles' makespan, ceil(rem*S /
+    // slots) rounds of 1/S of a tile (any count, not only powers of two:
+    // the Mixtral-shape down projection's last round of 80 tiles takes 3
+    // parts, 1043 -> 980 us).
+    int S = 1, best_r = 1, best_s = 1;
+    for (int s = 2; s <= p.max_split && rem * s <= p.max_slabs; ++s) {
+        const int r = (rem * s + p.slots - 1) / p.slots;
+        if (r * best_s < best_r * s) {
+            best_r = r;
+            best_s = s;
+            S = s;
+        }
+    }
     if (S < 2) return it;
     const int full = ntiles - rem;
     if (w < full) return it;
@@ -410,33 +421,48 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
         // S parts in part order (the sum does not depend on arrival order)
         // and runs the epilogue.  Layout: 16-byte chunk q4 of acc[i][j] of
         // thread tid at ((i * TB + j) * (AR / 4) + q4) * NT + tid.
+        //
+        // The parts may run on different XCDs, whose L2s are not coherent
+        // with each other.  The partials are therefore written and read at
+        // device scope (sc1: stores written through to the device coherence
+        // point, loads served from it), and each thread waits for its stores
+        // to complete before the workgroup barrier and the arrival count.
+        // This avoids a device-scope fence, which writes back this XCD's
+        // whole L2 and serialised badly when many parts arrive together
+        // (Mixtral-shape prefill: gate/up 1760 -> 1715 us, down 927 -> 864
+        // us; 32-row decode tiles: 160 -> 348 us with the fence).
         constexpr int PER_UNIT = BM * NB;
-        float *mine = p.part + ((int64_t)wi.unit * wi.S + wi.part) * PER_UNIT;
+        constexpr int kDeviceScope = 16;  // cache policy: sc1
+        const float *parts = p.part + (int64_t)wi.unit * wi.S * PER_UNIT;
+        const __amdgpu_buffer_rsrc_t prs = buffer_rsrc(parts, (int64_t)wi.S * PER_UNIT * 4);
+        const int mine = wi.part * PER_UNIT * 4;  // byte offset of this part's slab
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
             for (int j = 0; j < TB; ++j)
 #pragma unroll
                 for (int q4 = 0; q4 < AR / 4; ++q4) {
-                    f32x4 v = {acc[i][j][4 * q4], acc[i][j][4 * q4 + 1], acc[i][j][4 * q4 + 2], acc[i][j][4 * q4 + 3]};
-                    *(f32x4 *)(mine + (((i * TB + j) * (AR / 4) + q4) * NT + tid) * 4) = v;
+                    const f32x4 v = {acc[i][j][4 * q4], acc[i][j][4 * q4 + 1], acc[i][j][4 * q4 + 2],
+                                     acc[i][j][4 * q4 + 3]};
+                    const int o = (((i * TB + j) * (AR / 4) + q4) * NT + tid) * 16;
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), prs, o, mine, kDeviceScope);
                 }
-        __threadfence();
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's partial stores are complete
         __syncthreads();
         if (tid == 0) last_part = atomicAdd(p.cnt + wi.unit, 1) == wi.S - 1;
         __syncthreads();
         if (!last_part) return;
-        __threadfence();
-        const float *parts = p.part + (int64_t)wi.unit * wi.S * PER_UNIT;
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
             for (int j = 0; j < TB; ++j)
 #pragma unroll
                 for (int q4 = 0; q4 < AR / 4; ++q4) {
-                    const int64_t o = (((i * TB + j) * (AR / 4) + q4) * NT + tid) * 4;
-                    f32x4 v = *(const f32x4 *)(parts + o);
-                    for (int sp = 1; sp < wi.S; ++sp) v += *(const f32x4 *)(parts + (int64_t)sp * PER_UNIT + o);
+                    const int o = (((i * TB + j) * (AR / 4) + q4) * NT + tid) * 16;
+                    f32x4 v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(prs, o, 0, kDeviceScope));
+                    for (int sp = 1; sp < wi.S; ++sp)
+                        v += __builtin_bit_cast(
+                            f32x4, __builtin_amdgcn_raw_buffer_load_b128(prs, o, sp * PER_UNIT * 4, kDeviceScope));
                     acc[i][j][4 * q4] = v[0];
                     acc[i][j][4 * q4 + 1] = v[1];
                     acc[i][j][4 * q4 + 2] = v[2];
@@ -681,17 +707,15 @@ static void launch_bf16_t(const GemmArgs &a, hipStream_t s) {
     static_assert((int64_t)BM * NB <= kSplitUnitFloats, "split-K unit");
     auto kern = gemm_bf16_kernel<BM, BN, WM, WN, GLU, FB, PD, SB, IL, MF, RMAP, GSKIP>;
     GemmParams p{(const bf16 *)a.A, (const bf16 *)a.B0, (const bf16 *)a.B1, a.bias, (bf16 *)a.C,
-                 a.offsets, a.mstart, a.mtile, a.max_mt, a.G, a.rows, a.N, a.K, a.act, nullptr, nullptr, 0, 1,
+                 a.offsets, a.mstart, a.mtile, a.max_mt, a.G, a.rows, a.N, a.K, a.act, nullptr, nullptr, 0, 1, 0,
                  a.arow, a.a_rows * a.K * 2};
     int64_t grid = grid_for(a, BM, BN);
     if (grid == 0) return;
     // Split K of the last round needs the number of co-resident workgroups
-    // and room for that many partial tiles; otherwise it stays off.
-    // Only for the 256-row tiles and long K loops: each split tile pays a
-    // release/acquire pair (an L2 write-back and invalidate on this XCD)
-    // that short tiles do not amortise (measured slower on decode shapes).
+    // and room for that many partial tiles; otherwise it stays off.  Only
+    // for K loops of at least 64 tiles (at least 32 per part).
     const int KT = a.K / 64;
-    if (a.split.part != nullptr && BM == 256 && KT >= 64) {
+    if (a.split.part != nullptr && KT >= 64) {
         static int per_cu = -1;
         if (per_cu < 0) {
             int n = 0;
@@ -703,6 +727,7 @@ static void launch_bf16_t(const GemmArgs &a, hipStream_t s) {
             p.cnt = a.split.cnt;
             p.slots = (int)slots;
             p.max_split = std::min(8, KT / 32);
+            p.max_slabs = (int)std::min<int64_t>(a.split.part_floats / ((int64_t)BM * NB), 1 << 30);
             grid += (slots + kGridQuantum - 1) / kGridQuantum * kGridQuantum;
         }
     }
