@@ -715,7 +715,8 @@ static void launch_bf16_t(const GemmArgs &a, hipStream_t s) {
     // and room for that many partial tiles; otherwise it stays off.  Only
     // for K loops of at least 64 tiles (at least 32 per part).
     const int KT = a.K / 64;
-    if (a.split.part != nullptr && KT >= 64) {
+    constexpr int min_part = 32;  // K tiles per part at least (16 or 8 measured slower on decode tiles)
+    if (a.split.part != nullptr && KT >= 2 * min_part) {
         static int per_cu = -1;
         if (per_cu < 0) {
             int n = 0;
@@ -726,9 +727,13 @@ static void launch_bf16_t(const GemmArgs &a, hipStream_t s) {
             p.part = a.split.part;
             p.cnt = a.split.cnt;
             p.slots = (int)slots;
-            p.max_split = std::min(8, KT / 32);
+            p.max_split = std::min(8, KT / min_part);
             p.max_slabs = (int)std::min<int64_t>(a.split.part_floats / ((int64_t)BM * NB), 1 << 30);
-            grid += (slots + kGridQuantum - 1) / kGridQuantum * kGridQuantum;
+            // the split parts add rem * (S - 1) work items beyond the tiles,
+            // fewer than slots * (max_split - 1) and than max_slabs (rem * S
+            // slabs); surplus workgroups exit at once
+            const int64_t extra = std::min<int64_t>(slots * std::max(1, p.max_split - 1), p.max_slabs);
+            grid += (extra + kGridQuantum - 1) / kGridQuantum * kGridQuantum;
         }
     }
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * WM * WN), 0, s, p);

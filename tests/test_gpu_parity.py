@@ -194,6 +194,9 @@ SPLITK_SPECS = [
     workloads.MIXTRAL_PREFILL_BF16.replace(name="splitk_gemm1", T=700, d=4096, F=256),
     workloads.MIXTRAL_PREFILL_BF16.replace(name="splitk_gemm2_4_parts", T=700, d=256, F=8192),
     workloads.DEEPSEEK_SHARED_BF16.replace(name="splitk_shared_expert", T=520, d=4096, E=64, F=64, F_shared=256),
+    # 128-row tiles, about 100 down-projection tiles for 256 slots and a K loop of 160 tiles: 5 parts a tile,
+    # more split work items than slots
+    workloads.MIXTRAL_PREFILL_BF16.replace(name="splitk_parts_exceed_slots", T=1250, d=1024, E=25, k=1, F=10240),
 ]
 FFN_SPECS = FFN_SPECS + LONG_K_SPECS + SPLITK_SPECS
 
@@ -243,7 +246,7 @@ def test_expert_ffn_matches_oracle(spec):
         assert rel_err(_np(y_shared), ref) <= TOL[spec.dtype]
 
 
-@pytest.mark.parametrize("spec", [SPLITK_SPECS[0], SPLITK_SPECS[2]], ids=lambda s: s.name)
+@pytest.mark.parametrize("spec", [SPLITK_SPECS[0], SPLITK_SPECS[2], SPLITK_SPECS[3]], ids=lambda s: s.name)
 def test_split_k_forward_is_deterministic_and_matches_oracle(spec):
     inp = workloads.make_inputs(spec)
     dinp = to_dev(inp)
