@@ -116,8 +116,9 @@ struct GemmParams {
 // S = slots / rem parts along K, so that the last round is as wide as the
 // others and each part runs 1/S of the K loop.  The parts of a tile are
 // consecutive logical indices, mostly inside one run of 32 (one XCD); their
-// partial sums meet through device-scope fences, so parts that straddle two
-// XCDs are as correct.
+// partial sums are written and read at device scope, so parts that straddle
+// two XCDs are as correct.  rem * S may exceed the slots: the launch adds
+// workgroups for every part.
 struct WorkItem {
     int tile;    // logical tile
     int part;    // K part (0 when not split)
