@@ -53,7 +53,13 @@ __device__ inline void group_tile(int local, int mt, int ntn, int *m, int *n) {
 // The m-tile table holds, for every m-tile of the plan, its expert's first
 // m-tile (x), the expert index (y) and the expert's rows [z, w).  Tile t of the grid belongs to m-tile t / ntn,
 // so one table load (next to the total) places it; no search over experts.
-template <int BM>
+// UNIT > 0: the group's rows are cut into blocks of UNIT rows, and its mt
+// m-tiles take equal shares of the blocks (the first ones one more when they
+// do not divide evenly), instead of BM rows each and the remainder last.  An
+// expert of 1030 rows then runs five tiles of 13 row blocks of 16 instead of
+// four full tiles and one of 6 rows; with the row-block skip the padding
+// MFMAs all but vanish and the tiles of a group stay equally long.
+template <int BM, int UNIT = 0>
 __device__ inline TileCoord find_tile(int tile, const int32_t *offsets, const int32_t *mstart, const int4 *mtile,
                                       int max_mt, int G, int64_t rows, int ntn) {
     TileCoord c;
@@ -75,11 +81,20 @@ __device__ inline TileCoord find_tile(int tile, const int32_t *offsets, const in
     const int total = mstart[G];
     if (tile >= total * ntn) return c;
     const int local = tile - info.x * ntn;
-    group_tile(local, (int)((info.w - info.z + BM - 1) / BM), ntn, &m, &n);
+    const int mt_g = (int)((info.w - info.z + BM - 1) / BM);
+    group_tile(local, mt_g, ntn, &m, &n);
     c.g = info.y;
     c.nt = n;
-    c.row0 = info.z + (int64_t)m * BM;
-    c.row_end = info.w;
+    if constexpr (UNIT > 0) {
+        // blocks <= mt_g * BM / UNIT, so no m-tile gets more than BM rows
+        const int nblk = (info.w - info.z + UNIT - 1) / UNIT;
+        const int q = nblk / mt_g, r = nblk % mt_g;
+        c.row0 = info.z + (int64_t)UNIT * (m * q + min(m, r));
+        c.row_end = min((int64_t)info.w, info.z + (int64_t)UNIT * ((m + 1) * q + min(m + 1, r)));
+    } else {
+        c.row0 = info.z + (int64_t)m * BM;
+        c.row_end = info.w;
+    }
     c.valid = true;
     return c;
 }
@@ -163,15 +178,14 @@ __device__ inline int total_tiles(int BM, int ntn, const int32_t *offsets, const
     return mstart[G] * ntn;
 }
 
-// Calls f(std::integral_constant<int, NA>) with NA the smallest of 0, 1, 2, 4,
-// ..., TM that is at least n (TM a power of two).
+// Calls f(std::integral_constant<int, NA>) with NA = min(n, TM), n >= 0.
 template <int NA, int TM, typename F>
 __device__ inline void dispatch_active(int n, F &&f) {
     if constexpr (NA >= TM) {
         f(std::integral_constant<int, TM>{});
     } else {
         if (n <= NA) f(std::integral_constant<int, NA>{});
-        else dispatch_active<NA == 0 ? 1 : 2 * NA, TM>(n, f);
+        else dispatch_active<NA + 1, TM>(n, f);
     }
 }
 
@@ -186,8 +200,9 @@ __device__ inline void dispatch_active(int n, F &&f) {
 // power limit (2.06 vs 1.79 PFLOP/s in a register-only loop; 2.5% on the
 // whole grouped GEMM).
 // RMAP: waves w and w + 4, which share a SIMD, take different row halves (wm)
-// instead of the same one.  GSKIP: in a ragged last tile, run only the MFMAs
-// of the row blocks that hold rows of the expert.
+// instead of the same one.  GSKIP: balanced m-tiles (find_tile with UNIT =
+// MF), and in a tile of fewer than BM rows each wave runs only the MFMAs of
+// its row blocks that hold rows.
 template <int BM, int BN, int WM, int WN, bool GLU, bool FB, int PD = 2, bool SB = true, int IL = 0, int MF = 32,
           bool RMAP = false, bool GSKIP = true>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
@@ -215,7 +230,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
     const WorkItem wi = work_item(xcd_remap(blockIdx.x),
                                   total_tiles(BM, ntn, p.offsets, p.mstart, p.G, p.rows), p);
     if (!wi.valid) return;
-    const TileCoord tc = find_tile<BM>(wi.tile, p.offsets, p.mstart, p.mtile, p.max_mt, p.G, p.rows, ntn);
+    const TileCoord tc = find_tile<BM, GSKIP ? MF : 0>(wi.tile, p.offsets, p.mstart, p.mtile, p.max_mt, p.G,
+                                                        p.rows, ntn);
     if (!tc.valid) return;
     const int n0 = tc.nt * BN;
     const int64_t K = p.K;
@@ -227,10 +243,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
     const int tid = threadIdx.x;
     const int wave = tid / kWave, lane = tid % kWave;
     const int wm = RMAP ? wave / WN : wave % WM, wn = RMAP ? wave % WN : wave / WM;
-    // MF-row blocks of this wave that hold rows of the expert: in a ragged
-    // last tile a wave runs the MFMAs (and A-fragment reads) of only the
-    // first NA blocks, NA = that count rounded up to a power of two; blocks
-    // past it lie wholly past the expert's last row.
+    // MF-row blocks of this wave that hold rows of the tile: in a tile of
+    // fewer than BM rows a wave runs the MFMAs (and A-fragment reads) of only
+    // its first NA blocks; the blocks past them lie wholly past the tile's
+    // last row.
     const int64_t wrows = tc.row_end - (tc.row0 + (int64_t)wm * WTM);
     const int nact = wrows <= 0 ? 0 : (wrows >= WTM ? TM : (int)((wrows + MF - 1) / MF));
 
@@ -765,12 +781,15 @@ void launch_grouped_gemm(const GemmArgs &a, int shape, hipStream_t s) {
     // 32x32x16 on both GEMMs; row halves split across the two waves of a
     // SIMD (RMAP) 3% faster on the down projection and 1% slower on the
     // gate/up one; LDS reads interleaved 1:1 with the MFMAs (IL = 1) 2.5%
-    // faster on the down projection, no change on the gate/up one.  The
-    // row-block skip of ragged tiles (GSKIP) lets tiles finish unevenly, which
-    // breaks the lock-step of a 32-tile XCD group and doubled the L2 misses
-    // (3.1 -> 6.5 GB on the Mixtral gate/up GEMM) for about 1% of time; it is
-    // used only when groups average fewer than four full tiles of rows, where
-    // most tiles are ragged (DeepSeek-style layers).
+    // faster on the down projection, no change on the gate/up one.
+    // Balanced m-tiles with the row-block skip (GSKIP): gate/up 1865 -> 1790
+    // us, down 950 -> 884 us (the padding rows of each expert's last tile
+    // had been 13.5% of the MFMAs).  The skip alone, on tiles of BM rows
+    // and a short last one, had gained 1% and doubled the gate/up GEMM's L2
+    // misses: the short tiles finished early and broke the lock-step of a
+    // 32-tile XCD group.  Balanced tiles of one group are equally long, and
+    // the split rows (RMAP) give each SIMD one wave of each row half, so the
+    // skipped blocks shorten every SIMD's work alike.
     if (shape == kGemmDecode) {
         if (glu) launch_bf16_t<32, 128, 1, 4, true, true, 2, false, 32>(a, s);
         else launch_bf16_t<32, 128, 1, 4, false, true, 2, false, 32>(a, s);
@@ -779,16 +798,11 @@ void launch_grouped_gemm(const GemmArgs &a, int shape, hipStream_t s) {
         // (128 rows per expert) the down projection 112 -> 90 us, gate/up
         // 171 -> 165 us; on the Switch layer 41 -> 28 and 50 -> 38 us.
         // Splitting these short tiles along K measured 2x slower.
-        if (glu) launch_bf16_t<128, 128, 2, 4, true, true, 2, false, 32>(a, s);
-        else launch_bf16_t<128, 256, 2, 4, false, true, 2, false, 32>(a, s);
+        if (glu) launch_bf16_t<128, 128, 2, 4, true, true, 2, false, 32, true>(a, s);
+        else launch_bf16_t<128, 256, 2, 4, false, true, 2, false, 32, true>(a, s);
     } else {
-        if (a.ragged) {
-            if (glu) launch_bf16_t<256, 128, 2, 4, true, true, 2, false, 16, false, true, 0>(a, s);
-            else launch_bf16_t<256, 256, 2, 4, false, true, 2, false, 16, true, true, 1>(a, s);
-        } else {
-            if (glu) launch_bf16_t<256, 128, 2, 4, true, true, 2, false, 16, false, false, 0>(a, s);
-            else launch_bf16_t<256, 256, 2, 4, false, true, 2, false, 16, true, false, 1>(a, s);
-        }
+        if (glu) launch_bf16_t<256, 128, 2, 4, true, true, 2, false, 16, true, true, 0>(a, s);
+        else launch_bf16_t<256, 256, 2, 4, false, true, 2, false, 16, true, true, 1>(a, s);
     }
 }
 

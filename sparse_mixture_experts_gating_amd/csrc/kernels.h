@@ -114,7 +114,6 @@ struct GemmArgs {
     int act;                // ActKind; kActSwiglu uses B1
     bool bf16;
     SplitKWs split;         // bf16 only; part null = off
-    bool ragged;            // few rows per group on average: skip the MFMAs of row blocks past a group's end
     // bf16 only: A holds a_rows source rows, and row r of the grouped
     // operand is A row arow[r] (the routed token rows, gathered by the tile
     // loads themselves).  Needs a_rows * K * 2 < 2^31.

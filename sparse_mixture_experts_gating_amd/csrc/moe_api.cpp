@@ -397,14 +397,13 @@ moe_status do_ffn(const Derived &D, const void *x_perm, const void *x, const moe
     void *H = ws + fw.h;
     const SplitKWs split{D.bf16 ? (float *)(ws + fw.part) : nullptr, fw.part_floats,
                          D.bf16 ? (int32_t *)(ws + fw.cnt) : nullptr, fw.ncnt};
-    const bool ragged = plan.interleave;
     if (!plan_built)
         TRY(launch(K_TILE_PLAN, s, [&] {
             launch_tile_plan(r->counts, r->offsets, (int)D.E, plan.BM, mstart, mtile, fw.max_mt, split.cnt,
                              split.ncnt, plan.interleave, s);
         }));
     GemmArgs g1{x_perm, w->w1, w->w3, w->b1, H, r->offsets, mstart, mtile, fw.max_mt, (int)D.E, D.a_max, (int)D.F,
-                (int)D.d, D.act == MOE_ACT_SWIGLU ? kActSwiglu : D.act, D.bf16, split, ragged};
+                (int)D.d, D.act == MOE_ACT_SWIGLU ? kActSwiglu : D.act, D.bf16, split};
     if (x_perm == nullptr) {
         g1.A = x;
         g1.arow = r->row_token;
@@ -412,16 +411,16 @@ moe_status do_ffn(const Derived &D, const void *x_perm, const void *x, const moe
     }
     TRY(launch(K_GEMM1, s, [&] { launch_grouped_gemm(g1, shape, s); }));
     GemmArgs g2{H, w->w2, nullptr, w->b2, y_perm, r->offsets, mstart, mtile, fw.max_mt, (int)D.E, D.a_max, (int)D.d,
-                (int)D.F, kActNone, D.bf16, split, ragged};
+                (int)D.F, kActNone, D.bf16, split};
     TRY(launch(K_GEMM2, s, [&] { launch_grouped_gemm(g2, shape, s); }));
     if (D.Fs) {
         const int sshape = D.T <= 32 ? kGemmDecode : kGemmPrefill;
         void *Hs = ws + fw.hs;
         GemmArgs s1{x, w->ws1, w->ws3, nullptr, Hs, nullptr, nullptr, nullptr, 0, 1, D.T, (int)D.Fs, (int)D.d,
-                    kActSwiglu, D.bf16, split, false};
+                    kActSwiglu, D.bf16, split};
         TRY(launch(K_GEMM1_SHARED, s, [&] { launch_grouped_gemm(s1, sshape, s); }));
         GemmArgs s2{Hs, w->ws2, nullptr, nullptr, y_shared, nullptr, nullptr, nullptr, 0, 1, D.T, (int)D.d,
-                    (int)D.Fs, kActNone, D.bf16, split, false};
+                    (int)D.Fs, kActNone, D.bf16, split};
         TRY(launch(K_GEMM2_SHARED, s, [&] { launch_grouped_gemm(s2, sshape, s); }));
     }
     return MOE_OK;

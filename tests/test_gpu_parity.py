@@ -217,6 +217,12 @@ def test_expert_ffn_matches_oracle(spec):
         cap = oracle.capacity(spec.capacity_factor, spec.capacity_group, spec.E) if spec.gating == "switch" else 0
         p = oracle.permute(idx, spec.E, cap, spec.capacity_group)
         counts, row_token = p["counts"], p["row_token"]
+    _check_ffn(spec, inp, dinp, counts, row_token)
+
+
+def _check_ffn(spec, inp, dinp, counts, row_token):
+    """moe_expert_ffn on rows x[row_token] grouped by `counts` against the oracle's expert FFNs."""
+    cfg = moe.config_from_spec(spec)
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     r = moe.alloc_routing(cfg, DEV)
     r["counts"].copy_(torch.from_numpy(counts).to(DEV))
@@ -244,6 +250,29 @@ def test_expert_ffn_matches_oracle(spec):
     if spec.F_shared:
         ref = oracle.expert_ffn("swiglu", inp["x"], inp["ws1"], inp["ws3"], inp["ws2"])
         assert rel_err(_np(y_shared), ref) <= TOL[spec.dtype]
+
+
+# Row counts just past and below multiples of the tile height: each expert's
+# rows are cut into equal m-tiles of whole MFMA row blocks, and a wave skips
+# the blocks past its tile's last row.  256-row tiles (ragged plan with a
+# one-row expert among the others' m-tiles; plain plan) and 128-row tiles.
+BALANCED_CASES = [
+    (workloads.MIXTRAL_PREFILL_BF16.replace(name="balanced_256_ragged_plan", T=1024, d=512, E=4, F=512),
+     [257, 1030, 1, 760]),
+    (workloads.MIXTRAL_PREFILL_BF16.replace(name="balanced_256", T=2048, d=512, E=4, F=512),
+     [513, 1030, 17, 2536]),
+    (workloads.MIXTRAL_PREFILL_BF16.replace(name="balanced_128", T=2048, d=2048, E=16, k=1, F=512),
+     [129, 1, 257, 0, 300, 64, 96, 200, 33, 31, 150, 128, 159, 161, 99, 240]),
+]
+
+
+@pytest.mark.parametrize("spec,counts", BALANCED_CASES, ids=lambda c: getattr(c, "name", ""))
+def test_expert_ffn_balanced_tiles(spec, counts):
+    assert sum(counts) == spec.T * spec.k
+    inp = workloads.make_inputs(spec)
+    rng = np.random.default_rng(7)
+    row_token = rng.integers(0, spec.T, spec.T * spec.k).astype(np.int32)
+    _check_ffn(spec, inp, to_dev(inp), np.asarray(counts, np.int32), row_token)
 
 
 @pytest.mark.parametrize("spec", [SPLITK_SPECS[0], SPLITK_SPECS[2], SPLITK_SPECS[3]], ids=lambda s: s.name)
