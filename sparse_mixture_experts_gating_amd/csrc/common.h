@@ -106,5 +106,10 @@ __device__ inline u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, i
 // of row r is stored at chunk slot c ^ swz(r) so that the 16-byte reads of 16
 // consecutive rows at one chunk index touch distinct banks.
 __device__ inline int swz(int r) { return (r >> 1) & 7; }
+// Rows of BK bf16: 64 as above; 128 (sixteen chunks): slot c ^ (r % 16), so
+// that 16 consecutive rows at one chunk index touch distinct bank groups
+// whatever the bank count.  Both depend on r % 16 only.
+template <int BK>
+__device__ inline int swz_k(int r) { return BK == 64 ? swz(r) : (r & 15); }
 
 }  // namespace moe

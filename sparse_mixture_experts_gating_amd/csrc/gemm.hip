@@ -204,10 +204,11 @@ __device__ inline void dispatch_active(int n, F &&f) {
 // MF), and in a tile of fewer than BM rows each wave runs only the MFMAs of
 // its row blocks that hold rows.
 template <int BM, int BN, int WM, int WN, bool GLU, bool FB, int PD = 2, bool SB = true, int IL = 0, int MF = 32,
-          bool RMAP = false, bool GSKIP = true>
+          bool RMAP = false, bool GSKIP = true, int BK = 64>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
     constexpr int NT = 64 * WM * WN;  // threads
-    constexpr int BK = 64;
+    static_assert(BK == 64 || BK == 128, "K tile");
+    constexpr int KCH = BK / 8;  // 16-byte chunks per LDS operand row
     constexpr int NB = GLU ? 2 * BN : BN;
     constexpr int WTM = BM / WM, WTN = BN / WN;
     static_assert(MF == 32 || MF == 16, "MFMA shape");
@@ -217,10 +218,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
     using acc_t = float __attribute__((ext_vector_type(AR)));
     constexpr int TM = WTM / MF, TN = WTN / MF;
     constexpr int TB = GLU ? 2 * TN : TN;  // B fragments per k-substep (gate then up)
-    constexpr int RSTEP = NT / 8;          // rows between a thread's successive 16-byte chunks
+    constexpr int RSTEP = NT / KCH;        // rows between a thread's successive 16-byte chunks
     constexpr int A_PER_T = BM / RSTEP, B_PER_T = NB / RSTEP;
     constexpr int FS = FB ? 2 : 1;         // fragment register sets
     static_assert(A_PER_T >= 1 && B_PER_T >= 1 && BM % RSTEP == 0 && NB % RSTEP == 0, "tile/threads");
+    static_assert(RSTEP % 16 == 0, "a thread's rows share one LDS swizzle");
     static_assert(!GLU || BN % RSTEP == 0, "gate/up split must fall between a thread's chunks");
     static_assert(TM >= 1 && TN >= 1, "wave tile");
     __shared__ __attribute__((aligned(16))) bf16 lds[2][(BM + NB) * BK];
@@ -255,9 +257,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
     // each buffer ends at the expert's last row (A) or the matrix's last row
     // (B), so rows past it read as zeros: padding rows of a partial tile feed
     // the MFMAs zeros rather than copies of real rows, which keeps their
-    // switching power low.  Thread tid moves chunk (tid % 8) of rows
-    // tid/8 + RSTEP*i.
-    const int r0 = tid / 8, ch0 = tid % 8;
+    // switching power low.  Thread tid moves chunk (tid % KCH) of rows
+    // tid/KCH + RSTEP*i.
+    const int r0 = tid / KCH, ch0 = tid % KCH;
     const int64_t k0 = (int64_t)kbeg * BK;
     // Gathered A: one resource over all of A and a per-row byte offset from
     // the row map; padding rows get an offset past the limit (zeros).
@@ -284,12 +286,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
     // LDS: chunk c of row r sits at chunk slot c ^ swz(r); swz is the same for
     // all of a thread's rows (they differ by multiples of 16), so one base
     // address plus compile-time strides covers them.
-    const int sdst = r0 * BK + ((ch0 ^ swz(r0)) * 8);
+    const int sdst = r0 * BK + ((ch0 ^ swz_k<BK>(r0)) * 8);
     // MFMA operand lanes: lane l holds row (l % MF) of a fragment and the
     // 16-byte k chunk l / MF of the k-substep; rows of one wave's fragments
     // differ by multiples of 16, so they share one swizzle.
-    const int sw_a = swz(wm * WTM + lane % MF);
-    const int sw_b = swz(wn * WTN + lane % MF);
+    const int sw_a = swz_k<BK>(wm * WTM + lane % MF);
+    const int sw_b = swz_k<BK>(wn * WTN + lane % MF);
     const int fa0 = (wm * WTM + lane % MF) * BK, fb0 = (BM + wn * WTN + lane % MF) * BK;
 
     acc_t acc[TM][TB];
@@ -718,11 +720,11 @@ static int64_t grid_for(const GemmArgs &a, int BM, int BN) {
 }
 
 template <int BM, int BN, int WM, int WN, bool GLU, bool FB = true, int PD = 2, bool SB = false, int MF = 16,
-          bool RMAP = false, bool GSKIP = true, int IL = 0>
+          bool RMAP = false, bool GSKIP = true, int IL = 0, int BK = 64>
 static void launch_bf16_t(const GemmArgs &a, hipStream_t s) {
     constexpr int NB = GLU ? 2 * BN : BN;
     static_assert((int64_t)BM * NB <= kSplitUnitFloats, "split-K unit");
-    auto kern = gemm_bf16_kernel<BM, BN, WM, WN, GLU, FB, PD, SB, IL, MF, RMAP, GSKIP>;
+    auto kern = gemm_bf16_kernel<BM, BN, WM, WN, GLU, FB, PD, SB, IL, MF, RMAP, GSKIP, BK>;
     GemmParams p{(const bf16 *)a.A, (const bf16 *)a.B0, (const bf16 *)a.B1, a.bias, (bf16 *)a.C,
                  a.offsets, a.mstart, a.mtile, a.max_mt, a.G, a.rows, a.N, a.K, a.act, nullptr, nullptr, 0, 1, 0,
                  a.arow, a.a_rows * a.K * 2};
@@ -730,9 +732,9 @@ static void launch_bf16_t(const GemmArgs &a, hipStream_t s) {
     if (grid == 0) return;
     // Split K of the last round needs the number of co-resident workgroups
     // and room for that many partial tiles; otherwise it stays off.  Only
-    // for K loops of at least 64 tiles (at least 32 per part).
-    const int KT = a.K / 64;
-    constexpr int min_part = 32;  // K tiles per part at least (16 or 8 measured slower on decode tiles)
+    // for K loops of at least 4096 (at least 2048 per part).
+    const int KT = a.K / BK;
+    constexpr int min_part = 2048 / BK;  // K tiles per part at least (1024 or 512 measured slower on decode tiles)
     if (a.split.part != nullptr && KT >= 2 * min_part) {
         static int per_cu = -1;
         if (per_cu < 0) {
@@ -791,7 +793,14 @@ void launch_grouped_gemm(const GemmArgs &a, int shape, hipStream_t s) {
     // the split rows (RMAP) give each SIMD one wave of each row half, so the
     // skipped blocks shorten every SIMD's work alike.
     if (shape == kGemmDecode) {
-        if (glu) launch_bf16_t<32, 128, 1, 4, true, true, 2, false, 32>(a, s);
+        // gate/up: K tiles of 128 (256 bytes of each weight row per load
+        // round rather than 128: a plain read of the decode tile's weight
+        // rows in that pattern streams at 5.4 instead of 5.0 TB/s; Mixtral
+        // decode gate/up 355 -> 323 us).  The down projection stays on K
+        // tiles of 64: with 128 its LDS allows one workgroup per CU instead
+        // of three, and it measured 155 -> 166 us.
+        if (glu && a.K % 128 == 0) launch_bf16_t<32, 128, 1, 4, true, true, 2, false, 32, false, true, 0, 128>(a, s);
+        else if (glu) launch_bf16_t<32, 128, 1, 4, true, true, 2, false, 32>(a, s);
         else launch_bf16_t<32, 128, 1, 4, false, true, 2, false, 32>(a, s);
     } else if (shape == kGemmSmallM) {
         // 8 waves (2 per SIMD) rather than 4: on the expert-choice layer

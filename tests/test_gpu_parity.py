@@ -189,6 +189,8 @@ LONG_K_SPECS = [
     workloads.MIXTRAL_PREFILL_BF16.replace(name="long_k_prefill_tiles", T=1000, d=2048, F=1024),
     workloads.MIXTRAL_PREFILL_BF16.replace(name="long_k_small_m_tiles", T=1200, d=4096, E=16, k=1, F=512),
     workloads.MIXTRAL_PREFILL_BF16.replace(name="long_k_decode_tiles", T=16, d=2048, F=2048),
+    # decode gate/up on K tiles of 128 needs d % 128 == 0; d = 448 takes the 64 path
+    workloads.MIXTRAL_PREFILL_BF16.replace(name="decode_tiles_k_not_multiple_of_128", T=16, d=448, F=1024),
 ]
 SPLITK_SPECS = [
     workloads.MIXTRAL_PREFILL_BF16.replace(name="splitk_gemm1", T=700, d=4096, F=256),
