@@ -3,7 +3,10 @@
 // youngju.dev "Sparse Mixture of Experts（MoE）アーキテクチャ深層分析" (gating
 // formula), gathered per token instead of scattered with atomics, so the sum
 // runs in a fixed order (slot order; expert order for expert choice) and is
-// deterministic.  One wave per token, eight elements per lane per step.
+// deterministic.  One wave per token (or per column range of a token),
+// eight elements per lane per step.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -47,22 +50,28 @@ __device__ inline void store8<float>(float *p, const float *v) {
     store16(p + 4, b);
 }
 
-// The wave first compacts its token's kept slots (row >= 0) into LDS, in
-// slot order, with their gates; then, for each 8-element column chunk, it
-// issues the loads of up to kBatch kept rows at once and adds them in slot
-// order, so several loads are in flight per lane.
+// A wave owns one token's columns, or one of `parts` equal ranges of them
+// (few tokens: more waves in flight, shorter dependent load chains).  It
+// first compacts the token's kept slots (row >= 0) into LDS, in slot order,
+// with their gates; then, for each 8-element column chunk, it issues the
+// loads of up to kBatch kept rows at once and adds them in slot order, so
+// several loads are in flight per lane.
 constexpr int kMaxSlots = 1024;  // S <= E <= 1024
 constexpr int kBatch = 8;
 template <typename T>
 __global__ __launch_bounds__(256) void combine_kernel(const T *__restrict__ y_perm, const T *__restrict__ y_shared,
                                                       const float *__restrict__ w,
                                                       const int32_t *__restrict__ slot_row, int Tn, int d, int S,
-                                                      int expert_choice, T *__restrict__ y) {
+                                                      int expert_choice, int parts, T *__restrict__ y) {
     __shared__ int32_t krow[4][kMaxSlots];
     __shared__ float kw[4][kMaxSlots];
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+    const int64_t gw = (int64_t)blockIdx.x * 4 + wave;
+    const int64_t t = gw / parts;
     if (t >= Tn) return;
+    // columns [c_lo, c_hi) of this wave: whole 8-element chunks
+    const int cpp = (d / 8 + parts - 1) / parts * 8;
+    const int c_lo = (int)(gw % parts) * cpp, c_hi = min(d, c_lo + cpp);
     const int32_t *sr = slot_row + t * S;
     int nv = 0;
     for (int s0 = 0; s0 < S; s0 += kWave) {
@@ -80,7 +89,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const T *__restrict__ y_pe
     // lanes read entries other lanes wrote: one wave's LDS operations execute
     // in order, so only the compiler must not move the reads above the writes
     __builtin_amdgcn_wave_barrier();
-    for (int c0 = lane * 8; c0 < d; c0 += kWave * 8) {
+    for (int c0 = c_lo + lane * 8; c0 < c_hi; c0 += kWave * 8) {
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         for (int j0 = 0; j0 < nv; j0 += kBatch) {
             float v[kBatch][8];
@@ -107,14 +116,19 @@ __global__ __launch_bounds__(256) void combine_kernel(const T *__restrict__ y_pe
 
 void launch_combine(const CombineArgs &a, hipStream_t s) {
     if (a.T == 0) return;
-    const dim3 grid((a.T + 3) / 4);
+    // Column ranges per token: enough waves for about four per CU, each range
+    // at least one pass of the wave (512 columns).  Mixtral-shape decode (16
+    // tokens): 8 ranges.
+    const int64_t want = (4LL * device_cus() + a.T - 1) / a.T;
+    const int parts = (int)std::max<int64_t>(1, std::min<int64_t>(want, a.d / (kWave * 8)));
+    const dim3 grid((unsigned)((a.T * parts + 3) / 4));
     if (a.bf16)
         hipLaunchKernelGGL(combine_kernel<bf16>, grid, dim3(256), 0, s, (const bf16 *)a.y_perm,
-                           (const bf16 *)a.y_shared, a.w, a.slot_row, a.T, a.d, a.S, (int)a.expert_choice,
+                           (const bf16 *)a.y_shared, a.w, a.slot_row, a.T, a.d, a.S, (int)a.expert_choice, parts,
                            (bf16 *)a.y);
     else
         hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, s, (const float *)a.y_perm,
-                           (const float *)a.y_shared, a.w, a.slot_row, a.T, a.d, a.S, (int)a.expert_choice,
+                           (const float *)a.y_shared, a.w, a.slot_row, a.T, a.d, a.S, (int)a.expert_choice, parts,
                            (float *)a.y);
 }
 

@@ -287,7 +287,17 @@ def test_split_k_forward_is_deterministic_and_matches_oracle(spec):
     _check_layer(spec, inp, y1, routing, oracle.forward(spec, inp))
 
 
-@pytest.mark.parametrize("spec", workloads.SMALL, ids=lambda s: s.name)
+# Few tokens: each token's columns are split over several waves (ranges of
+# whole 8-element chunks; d = 1088 leaves a range of 544 and one of 544).
+COMBINE_SPECS = workloads.SMALL + [
+    workloads.MIXTRAL_DECODE_BF16.replace(name="combine_split_columns", T=5, d=1088),
+    workloads.DEEPSEEK_SHARED_BF16.replace(name="combine_split_columns_shared", T=3, d=4096, E=16, k=4),
+    workloads.BASIC_TOP2_F32.replace(name="combine_split_columns_f32", T=2, d=1536),
+    workloads.EXPERT_CHOICE_BF16.replace(name="combine_split_columns_ec", T=64, d=2048, E=4),
+]
+
+
+@pytest.mark.parametrize("spec", COMBINE_SPECS, ids=lambda s: s.name)
 def test_combine_matches_oracle(spec):
     inp = workloads.make_inputs(spec, experts=False)
     cfg = moe.config_from_spec(spec)
