@@ -207,6 +207,16 @@ def main():
     except RuntimeError as exc:  # capture not available: report the eager number only
         log(f"[bench] graph capture skipped: {exc}")
 
+    # per-step spread: each step between its own pair of events
+    per_step = []
+    for _ in range(args.steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        e1.synchronize()
+        per_step.append(e0.elapsed_time(e1))
+
     # per-kernel durations from HIP events recorded on the launch stream
     log("[bench] per-kernel event timing")
     moe.moe_timing_reset()
@@ -285,6 +295,11 @@ def main():
                    "activation": spec.act, "parallelism": "none (1 GPU)"},
         "layer_tflops_active": round(layer_tflops, 2),
         "layer_frac_bf16_peak": round(layer_tflops / PEAK_BF16_TFLOPS, 4),
+        "step_ms_median": round(float(np.median(per_step)), 4),
+        "step_ms_min": round(float(np.min(per_step)), 4),
+        # the kernels' event times per step, summed: within a few percent of
+        # ms_per_step when launch gaps are small
+        "stages_sum_ms": round(sum(v["avg_us"] * v["launches_per_step"] for v in kern.values()) / 1e3, 4),
         "cold_ms_per_step": round(cold_ms, 4),
         "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 4),
         "kernels_us": {n: v["avg_us"] for n, v in kern.items()},
