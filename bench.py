@@ -255,7 +255,8 @@ def main():
     # each step, outside the event pair
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     cold = []
-    for _ in range(max(3, min(args.steps, 10))):
+    n_cold = max(3, min(args.steps, 10))
+    for _ in range(n_cold):
         flush.fill_(1)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
@@ -263,8 +264,21 @@ def main():
         e1.record(stream)
         e1.synchronize()
         cold.append(e0.elapsed_time(e1))
-    del flush
     cold_ms = float(np.median(cold))
+    # the same, per kernel (the fill runs outside the library's event pairs)
+    moe.moe_timing_reset()
+    moe.moe_timing_enable(True)
+    for _ in range(n_cold):
+        flush.fill_(1)
+        step()
+    torch.cuda.synchronize()
+    kern_cold = {}
+    for i, n in enumerate(names):
+        tot, cnt = moe.moe_timing_read(i)
+        if cnt:
+            kern_cold[n] = round(tot * 1e3 / cnt, 3)
+    moe.moe_timing_enable(False)
+    del flush
 
     if args.copy_probe_mib:
         n = args.copy_probe_mib * (1 << 20)
@@ -303,6 +317,7 @@ def main():
         "cold_ms_per_step": round(cold_ms, 4),
         "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 4),
         "kernels_us": {n: v["avg_us"] for n, v in kern.items()},
+        "kernels_cold_us": kern_cold,
         "kernels": kern,
         "roofline": roofline,
         "cpu_baseline": cpu,
@@ -334,7 +349,15 @@ def cpu_baseline(spec, inp, seconds):
         if dt >= 0.6 * seconds or n == spec.T:
             break
         n = int(min(spec.T, max(2 * n, n * seconds / max(dt, 1e-3))))
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "host": {"cpu_model": model, "affinity_cpus": len(os.sched_getaffinity(0)), "nproc": os.cpu_count(),
+                     "omp_num_threads": os.environ.get("OMP_NUM_THREADS")},
             "sample": f"{n} of {spec.T} tokens of {spec.name}, all layer steps, float64 C loops "
                       f"(OpenMP over the rows of each expert), {dt:.1f} s"}
 
