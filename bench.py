@@ -290,6 +290,8 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(spec, inp, args.cpu_seconds)
+        # active GFLOP/s at the layer's average active work per token
+        cpu["gflops_active"] = round(cpu["value"] * flops / spec.T / 1e9, 3)
 
     out = {
         "metric": METRIC,
