@@ -783,7 +783,8 @@ void launch_grouped_gemm(const GemmArgs &a, int shape, hipStream_t s) {
     // 32x32x16 on both GEMMs; row halves split across the two waves of a
     // SIMD (RMAP) 3% faster on the down projection and 1% slower on the
     // gate/up one; LDS reads interleaved 1:1 with the MFMAs (IL = 1) 2.5%
-    // faster on the down projection, no change on the gate/up one.
+    // faster on the down projection, no change on the gate/up one (2%
+    // faster on it too once the m-tiles were balanced and split by rows).
     // Balanced m-tiles with the row-block skip (GSKIP): gate/up 1865 -> 1790
     // us, down 950 -> 884 us (the padding rows of each expert's last tile
     // had been 13.5% of the MFMAs).  The skip alone, on tiles of BM rows
@@ -810,7 +811,7 @@ void launch_grouped_gemm(const GemmArgs &a, int shape, hipStream_t s) {
         if (glu) launch_bf16_t<128, 128, 2, 4, true, true, 2, false, 32, true>(a, s);
         else launch_bf16_t<128, 256, 2, 4, false, true, 2, false, 32, true>(a, s);
     } else {
-        if (glu) launch_bf16_t<256, 128, 2, 4, true, true, 2, false, 16, true, true, 0>(a, s);
+        if (glu) launch_bf16_t<256, 128, 2, 4, true, true, 2, false, 16, true, true, 1>(a, s);
         else launch_bf16_t<256, 256, 2, 4, false, true, 2, false, 16, true, true, 1>(a, s);
     }
 }
