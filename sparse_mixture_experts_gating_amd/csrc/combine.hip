@@ -89,48 +89,28 @@ __global__ __launch_bounds__(256) void combine_kernel(const T *__restrict__ y_pe
     // lanes read entries other lanes wrote: one wave's LDS operations execute
     // in order, so only the compiler must not move the reads above the writes
     __builtin_amdgcn_wave_barrier();
-    // Two column chunks per pass: the loads of both are in flight together
-    // (a store waits for its data, so a chunk's loads would otherwise wait
-    // for the previous chunk's round trip).  Each element still sums its
-    // slots in slot order.
-    constexpr int CW = kWave * 8;  // columns one wave covers per chunk
-    for (int c0 = c_lo + lane * 8; c0 < c_hi; c0 += 2 * CW) {
-        const int c1 = c0 + CW;
-        const bool two = c1 < c_hi;
-        float acc0[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        float acc1[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int c0 = c_lo + lane * 8; c0 < c_hi; c0 += kWave * 8) {
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         for (int j0 = 0; j0 < nv; j0 += kBatch) {
-            float v0[kBatch][8], v1[kBatch][8] = {};  // v1 stays zero past the range
+            float v[kBatch][8];
 #pragma unroll
             for (int b = 0; b < kBatch; ++b)
-                if (j0 + b < nv) {
-                    const T *src = y_perm + (int64_t)krow[wave][j0 + b] * d;
-                    load8<T>(src + c0, v0[b]);
-                    if (two) load8<T>(src + c1, v1[b]);
-                }
+                if (j0 + b < nv) load8<T>(y_perm + (int64_t)krow[wave][j0 + b] * d + c0, v[b]);
 #pragma unroll
             for (int b = 0; b < kBatch; ++b)
                 if (j0 + b < nv) {
                     const float g = kw[wave][j0 + b];
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        acc0[i] = fmaf(g, v0[b][i], acc0[i]);
-                        acc1[i] = fmaf(g, v1[b][i], acc1[i]);
-                    }
+                    for (int i = 0; i < 8; ++i) acc[i] = fmaf(g, v[b][i], acc[i]);
                 }
         }
         if (y_shared) {
-            float v0[8], v1[8] = {};
-            load8<T>(y_shared + t * d + c0, v0);
-            if (two) load8<T>(y_shared + t * d + c1, v1);
+            float v[8];
+            load8<T>(y_shared + t * d + c0, v);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                acc0[i] += v0[i];
-                acc1[i] += v1[i];
-            }
+            for (int i = 0; i < 8; ++i) acc[i] += v[i];
         }
-        store8<T>(y + t * d + c0, acc0);
-        if (two) store8<T>(y + t * d + c1, acc1);
+        store8<T>(y + t * d + c0, acc);
     }
 }
 
