@@ -189,22 +189,20 @@ __device__ inline void dispatch_active(int n, F &&f) {
     }
 }
 
-// PD: K tiles in flight in registers (1: one set, loads issued a step ahead;
-// 2: two sets, loads issued two steps ahead).  SB: pin the loads at the head
-// of each step (scheduling barrier).  FB: double-buffer MFMA fragments.
+// Two K tiles are in flight in registers (loads issued two steps ahead) and
+// the MFMA fragments are double-buffered.  m-tiles are balanced (find_tile
+// with UNIT = MF), and in a tile of fewer than BM rows each wave runs only
+// the MFMAs of its row blocks that hold rows.
 // IL: 0 = compiler schedule; 1 = the next substep's LDS reads interleaved
-// 1:1 with this substep's MFMAs; 2 = all next-substep reads first, then the MFMAs.
+// 1:1 with this substep's MFMAs.
 // MF: MFMA tile edge, 32 (v_mfma_f32_32x32x16_bf16) or 16
 // (v_mfma_f32_16x16x32_bf16).  Both give the same flops per cycle, but with
 // switching operands the 16x16x32 form sustains more flops under the socket
 // power limit (2.06 vs 1.79 PFLOP/s in a register-only loop; 2.5% on the
 // whole grouped GEMM).
 // RMAP: waves w and w + 4, which share a SIMD, take different row halves (wm)
-// instead of the same one.  GSKIP: balanced m-tiles (find_tile with UNIT =
-// MF), and in a tile of fewer than BM rows each wave runs only the MFMAs of
-// its row blocks that hold rows.
-template <int BM, int BN, int WM, int WN, bool GLU, bool FB, int PD = 2, bool SB = true, int IL = 0, int MF = 32,
-          bool RMAP = false, bool GSKIP = true, int BK = 64>
+// instead of the same one.
+template <int BM, int BN, int WM, int WN, bool GLU, int IL = 0, int MF = 32, bool RMAP = false, int BK = 64>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
     constexpr int NT = 64 * WM * WN;  // threads
     static_assert(BK == 64 || BK == 128, "K tile");
@@ -220,7 +218,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
     constexpr int TB = GLU ? 2 * TN : TN;  // B fragments per k-substep (gate then up)
     constexpr int RSTEP = NT / KCH;        // rows between a thread's successive 16-byte chunks
     constexpr int A_PER_T = BM / RSTEP, B_PER_T = NB / RSTEP;
-    constexpr int FS = FB ? 2 : 1;         // fragment register sets
+    constexpr int FS = 2;                  // fragment register sets
     static_assert(A_PER_T >= 1 && B_PER_T >= 1 && BM % RSTEP == 0 && NB % RSTEP == 0, "tile/threads");
     static_assert(RSTEP % 16 == 0, "a thread's rows share one LDS swizzle");
     static_assert(!GLU || BN % RSTEP == 0, "gate/up split must fall between a thread's chunks");
@@ -232,7 +230,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
     const WorkItem wi = work_item(xcd_remap(blockIdx.x),
                                   total_tiles(BM, ntn, p.offsets, p.mstart, p.G, p.rows), p);
     if (!wi.valid) return;
-    const TileCoord tc = find_tile<BM, GSKIP ? MF : 0>(wi.tile, p.offsets, p.mstart, p.mtile, p.max_mt, p.G,
+    const TileCoord tc = find_tile<BM, MF>(wi.tile, p.offsets, p.mstart, p.mtile, p.max_mt, p.G,
                                                         p.rows, ntn);
     if (!tc.valid) return;
     const int n0 = tc.nt * BN;
@@ -347,31 +345,24 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0);
             }
     };
-    // MFMAs of one K tile whose k-substep-0 fragments are already in slot 0
+    // MFMAs of one K tile whose k-substep-0 fragments are already in slot 0:
+    // each substep first loads the next substep's fragments into the other
+    // slot, then runs its MFMAs
     auto compute = [&](const bf16 *L, auto na) {
         constexpr int NA = decltype(na)::value;
 #pragma unroll
         for (int ks = 0; ks < NSUB; ++ks) {
-            if constexpr (FB) {
-                if (ks + 1 < NSUB) fload(L, ks + 1, (ks + 1) & 1, na);
-                mfmas(ks & 1, na);
-                if constexpr (IL == 1) {
-                    if (ks + 1 < NSUB) {
+            if (ks + 1 < NSUB) fload(L, ks + 1, (ks + 1) & 1, na);
+            mfmas(ks & 1, na);
+            if constexpr (IL == 1) {
+                if (ks + 1 < NSUB) {
 #pragma unroll
-                        for (int g = 0; g < NA + TB; ++g) {
-                            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                        }
+                    for (int g = 0; g < NA + TB; ++g) {
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                     }
-                    __builtin_amdgcn_sched_barrier(0);
-                } else if constexpr (IL == 2) {
-                    if (ks + 1 < NSUB) __builtin_amdgcn_sched_group_barrier(0x100, NA + TB, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x008, NA * TB, 0);
-                    __builtin_amdgcn_sched_barrier(0);
                 }
-            } else {
-                if (ks > 0) fload(L, ks, 0, na);
-                mfmas(0, na);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     };
@@ -381,59 +372,37 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
     // wave meets every barrier).
     auto kloop = [&](auto na) {
         constexpr bool MMA = decltype(na)::value > 0;
-        if constexpr (PD == 1) {
-            // one register set: tile kt+1 is loaded during step kt and stored into
-            // the other LDS buffer at its end (the tail re-reads tile KT-1)
-            gload(0, 0);
-            lstore(0, 0);
+        gload(0, 0);
+        gload(KT > 1 ? 1 : 0, 1);
+        lstore(0, 0);
+        __syncthreads();
+        // Pairs of K tiles with no control flow inside, so the compiler's wait
+        // counts see exactly one register set in flight when the other is
+        // stored.  Loads and stores past the last tile re-read and re-store
+        // tile KT-1 into a buffer nobody reads afterwards.
+        int kt = 0;
+        for (; kt + 1 < KT; kt += 2) {
+            // even step: LDS buffer 0 holds tile kt, register set 1 holds tile kt+1
+            gload(min(kt + 2, KT - 1), 0);
+            if constexpr (MMA) fload(lds[0], 0, 0, na);
+            lstore(1, 1);
+            if constexpr (MMA) compute(lds[0], na);
             __syncthreads();
-            for (int kt = 0; kt < KT; ++kt) {
-                const int cur = kt & 1;
-                gload(min(kt + 1, KT - 1), 0);
-                if constexpr (SB) __builtin_amdgcn_sched_barrier(0);
-                if constexpr (MMA) {
-                    fload(lds[cur], 0, 0, na);
-                    compute(lds[cur], na);
-                }
-                lstore(cur ^ 1, 0);
-                __syncthreads();
-            }
-        } else {
-            gload(0, 0);
-            gload(KT > 1 ? 1 : 0, 1);
+            // odd step: LDS buffer 1 holds tile kt+1, register set 0 holds tile kt+2 (or KT-1)
+            gload(min(kt + 3, KT - 1), 1);
+            if constexpr (MMA) fload(lds[1], 0, 0, na);
             lstore(0, 0);
+            if constexpr (MMA) compute(lds[1], na);
             __syncthreads();
-            // Pairs of K tiles with no control flow inside, so the compiler's wait
-            // counts see exactly one register set in flight when the other is
-            // stored.  Loads and stores past the last tile re-read and re-store
-            // tile KT-1 into a buffer nobody reads afterwards.
-            int kt = 0;
-            for (; kt + 1 < KT; kt += 2) {
-                // even step: LDS buffer 0 holds tile kt, register set 1 holds tile kt+1
-                gload(min(kt + 2, KT - 1), 0);
-                if constexpr (SB) __builtin_amdgcn_sched_barrier(0);
-                if constexpr (MMA) fload(lds[0], 0, 0, na);
-                lstore(1, 1);
-                if constexpr (MMA) compute(lds[0], na);
-                __syncthreads();
-                // odd step: LDS buffer 1 holds tile kt+1, register set 0 holds tile kt+2 (or KT-1)
-                gload(min(kt + 3, KT - 1), 1);
-                if constexpr (SB) __builtin_amdgcn_sched_barrier(0);
-                if constexpr (MMA) fload(lds[1], 0, 0, na);
-                lstore(0, 0);
-                if constexpr (MMA) compute(lds[1], na);
-                __syncthreads();
-            }
-            if (kt < KT) {  // odd tile count: the last tile is in LDS buffer 0
-                if constexpr (MMA) {
-                    fload(lds[0], 0, 0, na);
-                    compute(lds[0], na);
-                }
+        }
+        if (kt < KT) {  // odd tile count: the last tile is in LDS buffer 0
+            if constexpr (MMA) {
+                fload(lds[0], 0, 0, na);
+                compute(lds[0], na);
             }
         }
     };
-    if constexpr (GSKIP) dispatch_active<0, TM>(nact, kloop);
-    else kloop(std::integral_constant<int, TM>{});
+    dispatch_active<0, TM>(nact, kloop);
 
     if (wi.S > 1) {
         // Publish this part's accumulators; the last part to arrive adds the
@@ -719,12 +688,11 @@ static int64_t grid_for(const GemmArgs &a, int BM, int BN) {
     return g;
 }
 
-template <int BM, int BN, int WM, int WN, bool GLU, bool FB = true, int PD = 2, bool SB = false, int MF = 16,
-          bool RMAP = false, bool GSKIP = true, int IL = 0, int BK = 64>
+template <int BM, int BN, int WM, int WN, bool GLU, int MF = 16, bool RMAP = false, int IL = 0, int BK = 64>
 static void launch_bf16_t(const GemmArgs &a, hipStream_t s) {
     constexpr int NB = GLU ? 2 * BN : BN;
     static_assert((int64_t)BM * NB <= kSplitUnitFloats, "split-K unit");
-    auto kern = gemm_bf16_kernel<BM, BN, WM, WN, GLU, FB, PD, SB, IL, MF, RMAP, GSKIP, BK>;
+    auto kern = gemm_bf16_kernel<BM, BN, WM, WN, GLU, IL, MF, RMAP, BK>;
     GemmParams p{(const bf16 *)a.A, (const bf16 *)a.B0, (const bf16 *)a.B1, a.bias, (bf16 *)a.C,
                  a.offsets, a.mstart, a.mtile, a.max_mt, a.G, a.rows, a.N, a.K, a.act, nullptr, nullptr, 0, 1, 0,
                  a.arow, a.a_rows * a.K * 2};
@@ -785,7 +753,7 @@ void launch_grouped_gemm(const GemmArgs &a, int shape, hipStream_t s) {
     // gate/up one; LDS reads interleaved 1:1 with the MFMAs (IL = 1) 2.5%
     // faster on the down projection, no change on the gate/up one (2%
     // faster on it too once the m-tiles were balanced and split by rows).
-    // Balanced m-tiles with the row-block skip (GSKIP): gate/up 1865 -> 1790
+    // Balanced m-tiles with the row-block skip: gate/up 1865 -> 1790
     // us, down 950 -> 884 us (the padding rows of each expert's last tile
     // had been 13.5% of the MFMAs).  The skip alone, on tiles of BM rows
     // and a short last one, had gained 1% and doubled the gate/up GEMM's L2
@@ -800,19 +768,19 @@ void launch_grouped_gemm(const GemmArgs &a, int shape, hipStream_t s) {
         // decode gate/up 355 -> 323 us).  The down projection stays on K
         // tiles of 64: with 128 its LDS allows one workgroup per CU instead
         // of three, and it measured 155 -> 166 us.
-        if (glu && a.K % 128 == 0) launch_bf16_t<32, 128, 1, 4, true, true, 2, false, 32, false, true, 0, 128>(a, s);
-        else if (glu) launch_bf16_t<32, 128, 1, 4, true, true, 2, false, 32>(a, s);
-        else launch_bf16_t<32, 128, 1, 4, false, true, 2, false, 32>(a, s);
+        if (glu && a.K % 128 == 0) launch_bf16_t<32, 128, 1, 4, true, 32, false, 0, 128>(a, s);
+        else if (glu) launch_bf16_t<32, 128, 1, 4, true, 32>(a, s);
+        else launch_bf16_t<32, 128, 1, 4, false, 32>(a, s);
     } else if (shape == kGemmSmallM) {
         // 8 waves (2 per SIMD) rather than 4: on the expert-choice layer
         // (128 rows per expert) the down projection 112 -> 90 us, gate/up
         // 171 -> 165 us; on the Switch layer 41 -> 28 and 50 -> 38 us.
         // Splitting these short tiles along K measured 2x slower.
-        if (glu) launch_bf16_t<128, 128, 2, 4, true, true, 2, false, 32, true>(a, s);
-        else launch_bf16_t<128, 256, 2, 4, false, true, 2, false, 32, true>(a, s);
+        if (glu) launch_bf16_t<128, 128, 2, 4, true, 32, true>(a, s);
+        else launch_bf16_t<128, 256, 2, 4, false, 32, true>(a, s);
     } else {
-        if (glu) launch_bf16_t<256, 128, 2, 4, true, true, 2, false, 16, true, true, 1>(a, s);
-        else launch_bf16_t<256, 256, 2, 4, false, true, 2, false, 16, true, true, 1>(a, s);
+        if (glu) launch_bf16_t<256, 128, 2, 4, true, 16, true, 1>(a, s);
+        else launch_bf16_t<256, 256, 2, 4, false, 16, true, 1>(a, s);
     }
 }
 
