@@ -201,8 +201,11 @@ __device__ inline void dispatch_active(int n, F &&f) {
 // power limit (2.06 vs 1.79 PFLOP/s in a register-only loop; 2.5% on the
 // whole grouped GEMM).
 // RMAP: waves w and w + 4, which share a SIMD, take different row halves (wm)
-// instead of the same one.
-template <int BM, int BN, int WM, int WN, bool GLU, int IL = 0, int MF = 32, bool RMAP = false, int BK = 64>
+// instead of the same one.  JOUT: MFMA order with the B fragment in the outer
+// loop (each B fragment feeds NA MFMAs in a row, the A fragments change every
+// MFMA) instead of the A fragment.
+template <int BM, int BN, int WM, int WN, bool GLU, int IL = 0, int MF = 32, bool RMAP = false, int BK = 64,
+          bool JOUT = false>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
     constexpr int NT = 64 * WM * WN;  // threads
     static_assert(BK == 64 || BK == 128, "K tile");
@@ -333,17 +336,25 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
             fb[slot][j] = __builtin_bit_cast(bf16x8,
                                              load16(Lb + ((j >= TN ? BN : 0) + (j % TN) * MF) * BK));
     };
+    auto mfma = [&](int slot, int i, int j) {
+        if constexpr (MF == 32)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0);
+        else
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0);
+    };
     auto mfmas = [&](int slot, auto na) {
         constexpr int NA = decltype(na)::value;
+        if constexpr (JOUT) {
 #pragma unroll
-        for (int i = 0; i < NA; ++i)
+            for (int j = 0; j < TB; ++j)
 #pragma unroll
-            for (int j = 0; j < TB; ++j) {
-                if constexpr (MF == 32)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0);
-                else
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0);
-            }
+                for (int i = 0; i < NA; ++i) mfma(slot, i, j);
+        } else {
+#pragma unroll
+            for (int i = 0; i < NA; ++i)
+#pragma unroll
+                for (int j = 0; j < TB; ++j) mfma(slot, i, j);
+        }
     };
     // MFMAs of one K tile whose k-substep-0 fragments are already in slot 0:
     // each substep first loads the next substep's fragments into the other
@@ -688,11 +699,12 @@ static int64_t grid_for(const GemmArgs &a, int BM, int BN) {
     return g;
 }
 
-template <int BM, int BN, int WM, int WN, bool GLU, int MF = 16, bool RMAP = false, int IL = 0, int BK = 64>
+template <int BM, int BN, int WM, int WN, bool GLU, int MF = 16, bool RMAP = false, int IL = 0, int BK = 64,
+          bool JOUT = false>
 static void launch_bf16_t(const GemmArgs &a, hipStream_t s) {
     constexpr int NB = GLU ? 2 * BN : BN;
     static_assert((int64_t)BM * NB <= kSplitUnitFloats, "split-K unit");
-    auto kern = gemm_bf16_kernel<BM, BN, WM, WN, GLU, IL, MF, RMAP, BK>;
+    auto kern = gemm_bf16_kernel<BM, BN, WM, WN, GLU, IL, MF, RMAP, BK, JOUT>;
     GemmParams p{(const bf16 *)a.A, (const bf16 *)a.B0, (const bf16 *)a.B1, a.bias, (bf16 *)a.C,
                  a.offsets, a.mstart, a.mtile, a.max_mt, a.G, a.rows, a.N, a.K, a.act, nullptr, nullptr, 0, 1, 0,
                  a.arow, a.a_rows * a.K * 2};
@@ -779,7 +791,7 @@ void launch_grouped_gemm(const GemmArgs &a, int shape, hipStream_t s) {
         if (glu) launch_bf16_t<128, 128, 2, 4, true, 32, true>(a, s);
         else launch_bf16_t<128, 256, 2, 4, false, 32, true>(a, s);
     } else {
-        if (glu) launch_bf16_t<256, 128, 2, 4, true, 16, true, 1>(a, s);
+        if (glu) launch_bf16_t<256, 128, 2, 4, true, 16, true, 1, 64, true>(a, s);
         else launch_bf16_t<256, 256, 2, 4, false, 16, true, 1>(a, s);
     }
 }
