@@ -15,6 +15,7 @@
 // panels), and every XCD receives runs of 32 consecutive tiles: a run shares
 // the expert's activation tiles and a few weight panels in that XCD's L2.
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "common.h"
@@ -669,13 +670,16 @@ void launch_tile_plan(const int32_t *counts, const int32_t *offsets, int E, int 
 
 int device_cus() {
     constexpr int kMaxDevices = 64;
-    static int cache[kMaxDevices] = {};
+    static std::atomic<int> cache[kMaxDevices] = {};  // 0: not yet queried
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
-    if (dev < kMaxDevices && cache[dev] > 0) return cache[dev];
+    if (dev < kMaxDevices) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    if (dev < kMaxDevices) cache[dev] = cus;
+    if (dev < kMaxDevices) cache[dev].store(cus, std::memory_order_relaxed);
     return cus;
 }
 
@@ -716,10 +720,14 @@ static void launch_bf16_t(const GemmArgs &a, hipStream_t s) {
     const int KT = a.K / BK;
     constexpr int min_part = 2048 / BK;  // K tiles per part at least (1024 or 512 measured slower on decode tiles)
     if (a.split.part != nullptr && KT >= 2 * min_part) {
-        static int per_cu = -1;
+        // workgroups of this kernel per CU, queried once (atomic: callers may
+        // launch from several host threads)
+        static std::atomic<int> per_cu_cache{-1};
+        int per_cu = per_cu_cache.load(std::memory_order_relaxed);
         if (per_cu < 0) {
             int n = 0;
             per_cu = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, 64 * WM * WN, 0) == hipSuccess ? n : 0;
+            per_cu_cache.store(per_cu, std::memory_order_relaxed);
         }
         const int64_t slots = (int64_t)device_cus() * per_cu;
         if (slots > 0 && slots <= a.split.ncnt && slots * BM * NB <= a.split.part_floats) {

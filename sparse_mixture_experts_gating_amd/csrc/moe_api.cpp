@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -46,7 +47,7 @@ struct Pending {
     int kind;
 };
 std::mutex g_tmu;
-bool g_timing = false;
+std::atomic<bool> g_timing{false};  // read outside the lock by every launch
 std::vector<Pending> g_pending;
 std::vector<hipEvent_t> g_pool;
 double g_total_ms[K_COUNT];
@@ -67,7 +68,7 @@ hipEvent_t take_event() {
 template <class F>
 moe_status launch(int kind, hipStream_t s, F &&f) {
     hipEvent_t a = nullptr, b = nullptr;
-    if (g_timing) {
+    if (g_timing.load(std::memory_order_relaxed)) {
         std::lock_guard<std::mutex> lk(g_tmu);
         a = take_event();
         b = take_event();
@@ -665,7 +666,7 @@ moe_status moe_forward(const moe_config *cfg, const void *x, const moe_weights *
 moe_status moe_timing_enable(int32_t on) {
     g_err.clear();
     std::lock_guard<std::mutex> lk(g_tmu);
-    g_timing = on != 0;
+    g_timing.store(on != 0, std::memory_order_relaxed);
     return MOE_OK;
 }
 
@@ -695,6 +696,10 @@ moe_status moe_timing_read(int32_t kind, double *total_ms, int64_t *launches) {
         float ms = 0.f;
         if (e == hipSuccess) e = hipEventElapsedTime(&ms, p.a, p.b);
         if (e != hipSuccess) {
+            for (auto &q : g_pending) {  // the events go back to the pool; their timings are lost
+                g_pool.push_back(q.a);
+                g_pool.push_back(q.b);
+            }
             g_pending.clear();
             return fail(MOE_ERR_HIP, "event timing failed: %s", hipGetErrorString(e));
         }
