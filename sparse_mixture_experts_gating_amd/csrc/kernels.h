@@ -62,6 +62,19 @@ struct TilePlanArgs {
     int ncnt;
     bool interleave;
 };
+
+// The router of a batch that fits one router block (bf16, token choice,
+// T <= 16, E <= 16) can also permute its selections in that block: it writes
+// what the permutation writes (counts, offsets, row_token, slot_row; the
+// first `capacity` per capacity group of group_chunks chunks kept) and the
+// tile plan when plan.mstart is set.
+struct RoutePermuteArgs {
+    int capacity = 0, group_chunks = 0;
+    int32_t *counts = nullptr, *offsets = nullptr, *row_token = nullptr, *slot_row = nullptr;
+    TilePlanArgs plan{};
+};
+bool route_permute_fits(int T, int E, bool bf16, bool expert_choice);
+void launch_route_permute(const RouteArgs &a, const RoutePermuteArgs &p, hipStream_t s);
 void launch_permute_small(const PermuteArgs &a, const TilePlanArgs &plan, hipStream_t s);
 void launch_permute_count(const PermuteArgs &a, hipStream_t s);
 void launch_permute_scan(const PermuteArgs &a, hipStream_t s);

@@ -654,11 +654,28 @@ moe_status moe_forward(const moe_config *cfg, const void *x, const moe_weights *
     void *x_perm = base + fw.x_perm;
     void *y_perm = base + fw.y_perm;
     void *y_shared = D.Fs ? base + fw.y_shared : nullptr;
-    TRY(do_route(D, x, w, &r, s));
     const bool fused = gather_in_gemm(D);
     const TilePlanArgs plan = plan_args(D, base, fw.ffn);
     bool plan_built = false;
-    TRY(do_permute(D, x, &r, x_perm, base, fw.perm, s, !fused, &plan, &plan_built));
+    if (fused && route_permute_fits((int)D.T, (int)D.E, D.bf16, D.ec)) {
+        // one router block: it also permutes its selections and writes the
+        // tile plan (Mixtral-shape decode: one launch fewer)
+        const RouteArgs a{x, w->w_router, w->b_router, (int)D.T, (int)D.d, (int)D.E, (int)D.k, D.gating, D.bf16,
+                          r.logits, r.topk_idx, r.topk_w, nullptr, nullptr};
+        RoutePermuteArgs pa;
+        pa.capacity = D.capacity;
+        pa.group_chunks = D.group_chunks;
+        pa.counts = r.counts;
+        pa.offsets = r.offsets;
+        pa.row_token = r.row_token;
+        pa.slot_row = r.slot_row;
+        pa.plan = plan;
+        TRY(launch(K_ROUTE, s, [&] { launch_route_permute(a, pa, s); }));
+        plan_built = true;
+    } else {
+        TRY(do_route(D, x, w, &r, s));
+        TRY(do_permute(D, x, &r, x_perm, base, fw.perm, s, !fused, &plan, &plan_built));
+    }
     TRY(do_ffn(D, fused ? nullptr : x_perm, x, &r, w, y_perm, y_shared, base, fw.ffn, s, plan_built));
     return do_combine(D, y_perm, y_shared, &r, y, s);
 }

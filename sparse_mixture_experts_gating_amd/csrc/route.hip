@@ -9,6 +9,7 @@
 //             gating formula, TopKGating, ExpertChoiceGating
 #include "common.h"
 #include "kernels.h"
+#include "perm_small.h"
 
 namespace moe {
 
@@ -91,12 +92,15 @@ __device__ inline float softplus(float u) { return fmaxf(u, 0.f) + log1pf(expf(-
 
 // NOISY adds the noise projection as a second MFMA accumulator set and forms
 // x.Wg + b + softplus(x.Wn) * noise ([yj-ja] TopKGating, training branch).
-template <int NT, int WK, bool NOISY>
+// PERM (a batch of one block, T <= 16): the block then permutes its own
+// selections (permute_small_block) and writes the tile plan, which saves
+// the permutation launch of a decode step.
+template <int NT, int WK, bool NOISY, bool PERM = false>
 __global__ __launch_bounds__(64 * WK) void route_bf16_kernel(
     const bf16 *__restrict__ x, const bf16 *__restrict__ wg, const float *__restrict__ bias,
     int T, int d, int E, int k, int gating, float *__restrict__ logits,
     int32_t *__restrict__ idx_out, float *__restrict__ w_out, const bf16 *__restrict__ wn,
-    const float *__restrict__ noise) {
+    const float *__restrict__ noise, RoutePermuteArgs perm) {
     constexpr int TOK = 16;
     constexpr int EP = 16 * NT;
     constexpr int LD = EP + 4;
@@ -188,6 +192,12 @@ __global__ __launch_bounds__(64 * WK) void route_bf16_kernel(
     for (int tt = wk; tt < TOK; tt += WK) {
         const int64_t t = tok0 + tt;
         if (t < T) gate_one_token(part + tt * LD, E, k, gating, t, idx_out, w_out);
+    }
+    if constexpr (PERM) {
+        extern __shared__ unsigned long long perm_lds[];
+        __syncthreads();  // every token's selection is written (and visible to the block)
+        permute_small_block<64 * WK>(idx_out, T, E, k, perm.capacity, perm.group_chunks, perm.counts,
+                                     perm.offsets, perm.row_token, perm.slot_row, perm.plan, perm_lds);
     }
 }
 
@@ -722,25 +732,39 @@ static void launch_router_tile(const RouteArgs &a, hipStream_t s) {
 }
 
 template <int NT, int WK>
-static void launch_route_bf16_wk(const RouteArgs &a, hipStream_t s) {
+static void launch_route_bf16_wk(const RouteArgs &a, const RoutePermuteArgs *perm, hipStream_t s) {
     const int grid = (a.T + 15) / 16;
-    if (a.wn)
+    if (perm) {  // one block (route_permute_fits): route, then permute in the same block
+        const size_t lds = (size_t)((a.T + kChunk - 1) / kChunk) * a.E * 16;
+        hipLaunchKernelGGL((route_bf16_kernel<NT, WK, false, true>), dim3(1), dim3(64 * WK), lds, s,
+                           (const bf16 *)a.x, (const bf16 *)a.wg, a.bias, a.T, a.d, a.E, a.k, a.gating, a.logits,
+                           a.idx, a.w, nullptr, nullptr, *perm);
+    } else if (a.wn) {
         hipLaunchKernelGGL((route_bf16_kernel<NT, WK, true>), dim3(grid), dim3(64 * WK), 0, s, (const bf16 *)a.x,
                            (const bf16 *)a.wg, a.bias, a.T, a.d, a.E, a.k, a.gating, a.logits, a.idx, a.w,
-                           (const bf16 *)a.wn, a.noise);
-    else
+                           (const bf16 *)a.wn, a.noise, RoutePermuteArgs{});
+    } else {
         hipLaunchKernelGGL((route_bf16_kernel<NT, WK, false>), dim3(grid), dim3(64 * WK), 0, s, (const bf16 *)a.x,
                            (const bf16 *)a.wg, a.bias, a.T, a.d, a.E, a.k, a.gating, a.logits, a.idx, a.w,
-                           nullptr, nullptr);
+                           nullptr, nullptr, RoutePermuteArgs{});
+    }
 }
 
 // K-split depth: 16 waves once each holds at least eight 32-wide chunks.
 template <int NT>
-static void launch_route_bf16_t(const RouteArgs &a, hipStream_t s) {
+static void launch_route_bf16_t(const RouteArgs &a, hipStream_t s, const RoutePermuteArgs *perm = nullptr) {
     const int nk = a.d / 32;
-    if (nk >= 128) launch_route_bf16_wk<NT, 16>(a, s);
-    else if (nk >= 32) launch_route_bf16_wk<NT, 8>(a, s);
-    else launch_route_bf16_wk<NT, 4>(a, s);
+    if (nk >= 128) launch_route_bf16_wk<NT, 16>(a, perm, s);
+    else if (nk >= 32) launch_route_bf16_wk<NT, 8>(a, perm, s);
+    else launch_route_bf16_wk<NT, 4>(a, perm, s);
+}
+
+bool route_permute_fits(int T, int E, bool bf16, bool expert_choice) {
+    return bf16 && !expert_choice && T >= 1 && T <= 16 && E <= 16;
+}
+
+void launch_route_permute(const RouteArgs &a, const RoutePermuteArgs &p, hipStream_t s) {
+    launch_route_bf16_t<1>(a, s, &p);
 }
 
 void launch_route(const RouteArgs &a, hipStream_t s) {

@@ -164,3 +164,40 @@ def test_forward_gather_in_gemm_equals_step_path(spec):
     assert torch.equal(r_fwd["offsets"], r_steps["offsets"])
     assert torch.equal(r_fwd["row_token"][:n], r_steps["row_token"][:n])
     assert torch.equal(y_fwd, y_steps)
+
+
+# A batch that fits one router block (bf16 token choice, T <= 16, E <= 16):
+# in moe_forward that block also permutes its selections and writes the tile
+# plan, so no permutation or plan kernel runs.  Its routing buffers and output
+# equal the step path's bit for bit (1024-, 512- and 256-thread router blocks;
+# Switch drops; one token).
+ONE_BLOCK_SPECS = [
+    workloads.MIXTRAL_DECODE_BF16.replace(name="one_block_d4096", d=4096, F=256),
+    workloads.MIXTRAL_DECODE_BF16.replace(name="one_block_d1024_k4", d=1024, E=16, k=4, F=256),
+    workloads.MIXTRAL_DECODE_BF16.replace(name="one_block_d512_t7", T=7, d=512, F=256),
+    workloads.MIXTRAL_DECODE_BF16.replace(name="one_block_t1", T=1, d=512, F=256),
+    workloads.SWITCH_TOP1_BF16.replace(name="one_block_switch_drops", T=16, d=512, E=4, F=256, capacity_factor=1.0,
+                                       capacity_group=0),
+]
+
+
+@pytest.mark.parametrize("spec", ONE_BLOCK_SPECS, ids=lambda s: s.name)
+def test_one_block_router_permutes_its_own_selections(spec):
+    from gpu_harness import run_forward
+    dinp = to_dev(workloads.make_inputs(spec))
+    moe.moe_timing_reset()
+    moe.moe_timing_enable(True)
+    y_fwd, r_fwd = run_forward(spec, dinp)
+    names = moe.moe_kernel_names()
+    launched = {n for i, n in enumerate(names) if moe.moe_timing_read(i)[1]}
+    moe.moe_timing_enable(False)
+    assert "route" in launched
+    assert not launched & {"permute_small", "permute_count", "permute_scan", "permute_scatter", "tile_plan"}
+    y_steps, r_steps = _run_steps(spec, dinp, noisy=False)
+    n = int(r_fwd["offsets"][-1])
+    for key in ("topk_idx", "topk_w", "counts", "offsets", "slot_row"):
+        assert torch.equal(r_fwd[key], r_steps[key]), key
+    assert torch.equal(r_fwd["row_token"][:n], r_steps["row_token"][:n])
+    assert torch.equal(y_fwd, y_steps)
+    if spec.gating == "switch":
+        assert (r_fwd["slot_row"] < 0).any()  # the capacity dropped some tokens
