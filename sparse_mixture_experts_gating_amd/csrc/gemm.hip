@@ -785,19 +785,22 @@ void launch_grouped_gemm(const GemmArgs &a, int shape, hipStream_t s) {
         // gate/up: K tiles of 128 (256 bytes of each weight row per load
         // round rather than 128: a plain read of the decode tile's weight
         // rows in that pattern streams at 5.4 instead of 5.0 TB/s; Mixtral
-        // decode gate/up 355 -> 323 us).  The down projection stays on K
-        // tiles of 64: with 128 its LDS allows one workgroup per CU instead
-        // of three, and it measured 155 -> 166 us.
-        if (glu && a.K % 128 == 0) launch_bf16_t<32, 128, 1, 4, true, 32, false, 0, 128>(a, s);
-        else if (glu) launch_bf16_t<32, 128, 1, 4, true, 32>(a, s);
+        // decode gate/up 355 -> 323 us) and LDS reads interleaved with the
+        // MFMAs (324 -> 318 us).  The down projection stays on K tiles of 64
+        // (with 128 its LDS allows one workgroup per CU instead of three:
+        // 155 -> 166 us) and on the compiler's schedule (interleaved: Switch
+        // down projection 17.5 -> 18.3 us).
+        if (glu && a.K % 128 == 0) launch_bf16_t<32, 128, 1, 4, true, 32, false, 1, 128>(a, s);
+        else if (glu) launch_bf16_t<32, 128, 1, 4, true, 32, false, 1>(a, s);
         else launch_bf16_t<32, 128, 1, 4, false, 32>(a, s);
     } else if (shape == kGemmSmallM) {
         // 8 waves (2 per SIMD) rather than 4: on the expert-choice layer
         // (128 rows per expert) the down projection 112 -> 90 us, gate/up
         // 171 -> 165 us; on the Switch layer 41 -> 28 and 50 -> 38 us.
-        // Splitting these short tiles along K measured 2x slower.
-        if (glu) launch_bf16_t<128, 128, 2, 4, true, 32, true>(a, s);
-        else launch_bf16_t<128, 256, 2, 4, false, 32, true>(a, s);
+        // Splitting these short tiles along K measured 2x slower.  LDS reads
+        // interleaved with the MFMAs: expert-choice GEMMs about -1%.
+        if (glu) launch_bf16_t<128, 128, 2, 4, true, 32, true, 1>(a, s);
+        else launch_bf16_t<128, 256, 2, 4, false, 32, true, 1>(a, s);
     } else {
         if (glu) launch_bf16_t<256, 128, 2, 4, true, 16, true, 1, 64, true>(a, s);
         else launch_bf16_t<256, 256, 2, 4, false, 16, true, 1>(a, s);
