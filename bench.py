@@ -287,9 +287,9 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
 
-    cpu = None
+    cpu = parity = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(spec, inp, args.cpu_seconds)
+        cpu, parity = cpu_baseline(spec, inp, args.cpu_seconds, y, routing)
         # active GFLOP/s at the layer's average active work per token
         cpu["gflops_active"] = round(cpu["value"] * flops / spec.T / 1e9, 3)
 
@@ -322,14 +322,31 @@ def main():
         "kernels_cold_us": kern_cold,
         "kernels": kern,
         "roofline": roofline,
+        "routing": routing_summary(spec, counts),
+        "parity": parity,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(spec, inp, seconds):
+def routing_summary(spec, counts):
+    """Realised expert load of the timed batch: rows per expert, max over
+    mean, experts that received no row, and assignments the capacity dropped."""
+    import numpy as np
+    c = np.asarray(counts, np.int64)
+    slots = int(c.sum()) if spec.gating == "expert_choice" else spec.T * spec.k
+    return {"rows": int(c.sum()), "rows_per_expert_max": int(c.max()), "rows_per_expert_mean": round(float(c.mean()), 3),
+            "load_max_over_mean": round(float(c.max() / max(c.mean(), 1e-30)), 3),
+            "empty_experts": int((c == 0).sum()), "dropped_assignments": int(slots - c.sum())}
+
+
+def cpu_baseline(spec, inp, seconds, y_gpu, routing):
     """The oracle as it stands on the host cores, on a bounded sample of tokens
-    of the same workload (host copies of the same inputs)."""
+    of the same workload (host copies of the same inputs).  The same leg then
+    checks the timed batch against the oracle: the sampled tokens' outputs
+    with the oracle routed by the GPU's own logits (routing-locked) and by its
+    own logits (independent, flipped tokens left out), and the routing flips
+    over every token.  Returns (cpu_baseline, parity)."""
     import numpy as np
     import torch
 
@@ -357,11 +374,62 @@ def cpu_baseline(spec, inp, seconds):
             model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
     except OSError:
         pass
-    return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "host": {"cpu_model": model, "affinity_cpus": len(os.sched_getaffinity(0)), "nproc": os.cpu_count(),
-                     "omp_num_threads": os.environ.get("OMP_NUM_THREADS")},
-            "sample": f"{n} of {spec.T} tokens of {spec.name}, all layer steps, float64 C loops "
-                      f"(OpenMP over the rows of each expert), {dt:.1f} s"}
+    cpu = {"value": round(n / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "host": {"cpu_model": model, "affinity_cpus": len(os.sched_getaffinity(0)), "nproc": os.cpu_count(),
+                    "omp_num_threads": os.environ.get("OMP_NUM_THREADS")},
+           "sample": f"{n} of {spec.T} tokens of {spec.name}, all layer steps, float64 C loops "
+                     f"(OpenMP over the rows of each expert), {dt:.1f} s"}
+    return cpu, parity_check(spec, host, toks, y_gpu, routing)
+
+
+def parity_check(spec, host, toks, y_gpu, routing):
+    """Oracle checks of the timed batch (part of the CPU leg)."""
+    import numpy as np
+
+    import oracle
+
+    log("[bench] parity: oracle on the GPU's logits and on its own")
+    T, E = spec.T, spec.E
+    y = y_gpu[__import__("torch").from_numpy(toks).to(y_gpu.device)].float().cpu().numpy().astype(np.float64)
+    glg = routing["logits"].cpu().numpy().reshape(T, E)
+    gidx = routing["topk_idx"].cpu().numpy()
+
+    def rel(a, b):
+        return float(np.abs(a - b).max() / max(np.abs(b).max(), 1e-300)) if len(a) else 0.0
+
+    locked = oracle.forward_tokens(spec, host, toks, lg=glg)
+    olg = oracle.logits(host["x"], host["wg"], host["bg"])
+    out = {"sampled_tokens": int(len(toks)), "max_rel_err_routing_locked": rel(y, locked["y64"]),
+           "max_abs_logit_diff": float(np.abs(glg.astype(np.float64) - olg).max())}
+    if spec.gating == "expert_choice":
+        C = oracle.capacity(spec.capacity_factor, T, E)
+        oidx, _ = oracle.route_expert_choice(olg, C)
+        g = gidx.reshape(E, C)
+        diff = [set(g[e].tolist()) ^ set(oidx[e].tolist()) for e in range(E)]
+        flipped = set().union(*diff)
+        out.update(flipped_experts=sum(1 for d_ in diff if d_), flipped_tokens=len(flipped))
+        keep = ~np.isin(toks, list(flipped))
+    else:
+        k = spec.k
+        oidx, _ = oracle.route_topk(olg, k, spec.gating)
+        g = gidx.reshape(T, k)
+        flips = (np.sort(g, 1) != np.sort(oidx, 1)).any(1)
+        out.update(flipped_tokens=int(flips.sum()))
+        keep = ~flips[toks]
+        if spec.gating == "switch" or spec.capacity_factor > 0:
+            # a flip moves later tokens of its (group, expert) too: leave out
+            # every sampled token whose kept slots differ
+            cap = oracle.capacity_topk(spec.capacity_factor, spec.capacity_group or T, k, E, spec.min_capacity)
+            grp = spec.capacity_group
+            kg = np.where(oracle.permute(g, E, cap, grp)["slot_row"] >= 0, g, -1)
+            ko = np.where(oracle.permute(oidx, E, cap, grp)["slot_row"] >= 0, oidx, -1)
+            moved = (np.sort(kg, 1) != np.sort(ko, 1)).any(1)
+            out.update(flip_affected_tokens=int(moved.sum()))
+            keep &= ~moved[toks]
+    indep = oracle.forward_tokens(spec, host, toks[keep]) if keep.any() else None
+    out["max_rel_err_independent"] = rel(y[keep], indep["y64"]) if indep is not None else None
+    out["tolerance"] = 1e-5 if spec.dtype == "f32" else 1e-2
+    return out
 
 
 if __name__ == "__main__":

@@ -80,10 +80,30 @@ INT_SPECS = [s.replace(name=s.name + "_int", inputs="integer") for s in workload
                                            inputs="integer"),
     workloads.DEEPSEEK_SHARED_BF16.replace(name="router_e256_t32768_int", T=32768, d=128, E=256, k=8, F=64,
                                            F_shared=0, inputs="integer"),
+    # one router block that also permutes its selections inside moe_forward
+    # (bf16 token choice, T <= 16, E <= 16): the Mixtral decode router at
+    # d = 4096 (16 waves), and a Switch batch whose capacity drops tokens
+    workloads.MIXTRAL_DECODE_BF16.replace(name="one_block_decode_d4096_int", F=256, inputs="integer"),
+    workloads.SWITCH_TOP1_BF16.replace(name="one_block_switch_drops_int", T=16, d=512, E=4, F=256,
+                                       capacity_factor=1.0, capacity_group=0, inputs="integer"),
 ]
 
 
-@pytest.mark.parametrize("spec", INT_SPECS, ids=lambda s: s.name)
+# The router variants the full-size layers run, at their real K depth and
+# token counts (integer inputs keep every product and sum exact): the
+# 16-wave K split (d >= 4096, Mixtral prefill router), the 8-wave one
+# (1024 <= d < 4096), the LDS-staged tile router with 256 expert columns at
+# d = 7168 over 8192 tokens (DeepSeek-style router), and with 64 columns at
+# the expert-choice layer's shape.
+ROUTER_DEPTH_SPECS = [
+    workloads.MIXTRAL_PREFILL_BF16.replace(name="router_16_waves_d4096_t4096_int", inputs="integer"),
+    workloads.SWITCH_TOP1_BF16.replace(name="router_8_waves_d2048_e16_int", d=2048, inputs="integer"),
+    workloads.DEEPSEEK_SHARED_BF16.replace(name="router_tile_d7168_e256_t8192_int", inputs="integer"),
+    workloads.EXPERT_CHOICE_BF16.replace(name="router_tile_d2048_e64_t8192_ec_int", inputs="integer"),
+]
+
+
+@pytest.mark.parametrize("spec", INT_SPECS + ROUTER_DEPTH_SPECS, ids=lambda s: s.name)
 def test_fused_route_bit_exact_on_exact_inputs(spec):
     inp = workloads.make_inputs(spec, experts=False)
     dinp = to_dev(inp)
@@ -200,7 +220,33 @@ SPLITK_SPECS = [
     # more split work items than slots
     workloads.MIXTRAL_PREFILL_BF16.replace(name="splitk_parts_exceed_slots", T=1250, d=1024, E=25, k=1, F=10240),
 ]
-FFN_SPECS = FFN_SPECS + LONG_K_SPECS + SPLITK_SPECS
+# Combinations the ABI accepts beyond the six layers: expert biases on the
+# bf16 MFMA path (ReLU and GELU epilogues, 256-, 128- and 32-row tiles), the
+# float32 SwiGLU and GELU experts, softmax-then-top-k gating without
+# renormalisation end to end, and float32 shared-expert and expert-choice
+# layers.
+ABI_SPECS = [
+    workloads.BASIC_TOP2_F32.replace(name="relu_bias_bf16_256_row_tiles", dtype="bf16", T=2000, d=256, F=384),
+    workloads.BASIC_TOP2_F32.replace(name="relu_bias_bf16_128_row_tiles", dtype="bf16", T=1200, d=256, E=16, k=2,
+                                     F=8192),
+    workloads.BASIC_TOP2_F32.replace(name="relu_bias_bf16_decode", dtype="bf16", T=16, d=256, F=384),
+    workloads.SWITCH_TOP1_BF16.replace(name="gelu_bias_bf16_switch", T=640, d=256, F=640, capacity_group=320,
+                                       expert_bias=True),
+    workloads.MIXTRAL_PREFILL_BF16.replace(name="gelu_bf16_top2_no_bias", act="gelu", T=900, d=256, F=320),
+    workloads.MIXTRAL_PREFILL_BF16.replace(name="swiglu_f32", dtype="f32", T=300, d=128, F=192),
+    workloads.SWITCH_TOP1_BF16.replace(name="gelu_f32_switch", dtype="f32", T=640, d=128, F=256,
+                                       capacity_group=320),
+    workloads.SWITCH_TOP1_BF16.replace(name="gelu_bias_f32_top2", dtype="f32", gating="topk_softmax", k=2,
+                                       T=300, d=128, F=256, capacity_factor=0.0, capacity_group=0,
+                                       expert_bias=True),
+    workloads.MIXTRAL_PREFILL_BF16.replace(name="softmax_topk_bf16", gating="softmax_topk", T=500, d=256, E=16,
+                                           k=4, F=256),
+    workloads.BASIC_TOP2_F32.replace(name="softmax_topk_f32_relu_bias", gating="softmax_topk", T=203),
+    workloads.DEEPSEEK_SHARED_BF16.replace(name="shared_expert_f32", dtype="f32", T=200, d=128, E=32, k=4, F=64,
+                                           F_shared=96),
+    workloads.EXPERT_CHOICE_BF16.replace(name="expert_choice_f32", dtype="f32", T=500, d=128, E=8, F=96),
+]
+FFN_SPECS = FFN_SPECS + LONG_K_SPECS + SPLITK_SPECS + ABI_SPECS
 
 
 @pytest.mark.parametrize("spec", FFN_SPECS, ids=lambda s: s.name)
@@ -377,7 +423,7 @@ def _check_layer(spec, inp, y, routing, ref):
     return (~ok).sum()
 
 
-@pytest.mark.parametrize("spec", workloads.SMALL, ids=lambda s: s.name)
+@pytest.mark.parametrize("spec", workloads.SMALL + ABI_SPECS, ids=lambda s: s.name)
 def test_forward_matches_oracle(spec):
     inp = workloads.make_inputs(spec)
     y, routing = run_forward(spec, to_dev(inp))
