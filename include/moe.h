@@ -196,6 +196,26 @@ moe_status moe_route_from_logits(const moe_config *cfg, const float *logits,
 moe_status moe_permute(const moe_config *cfg, const void *x, moe_routing *routing,
                        void *x_perm, void *ws, size_t ws_bytes, void *stream);
 
+/* moe_permute for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * no workspace argument.  The scratch space moe_permute takes from `ws`
+ * (per-chunk expert counts, prefixes and bases, per-assignment ranks) comes
+ * from a fixed array in the library's own device memory instead, of
+ * MOE_PERMUTE_NOALLOC_SCRATCH_BYTES per GPU, allocated when the library's
+ * code is loaded on that GPU and held until the process ends.  Calls no
+ * hipMalloc/hipFree and records no timing events.  A configuration whose
+ * MOE_STAGE_PERMUTE workspace exceeds that size returns MOE_ERR_UNSUPPORTED
+ * before any launch (8 MiB holds, e.g., T = 65536 tokens with k = 8 of
+ * E = 256 experts).  Every call on one GPU shares that GPU's array: calls
+ * that overlap on one GPU (on different streams, or from host threads that
+ * do not order them) race and give undefined results.  Each call writes
+ * every scratch entry it reads, so nothing carries over from the previous
+ * call.  `stream` must belong to the current device.  Arguments, results
+ * and errors otherwise as moe_permute. */
+#define MOE_PERMUTE_NOALLOC_SCRATCH_BYTES (8u << 20)
+moe_status moe_permute_noalloc(const moe_config *cfg, const void *x, moe_routing *routing, void *x_perm,
+                               void *stream);
+
 /* Expert FFNs as grouped GEMMs over the expert-contiguous rows: y_perm [A_max][d]
  * (dtype) for rows < offsets[E]; y_shared [T][d] (dtype) = shared expert of x
  * when cfg->d_ff_shared > 0 (x: device [T][d], else may be NULL).  Only the

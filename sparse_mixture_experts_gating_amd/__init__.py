@@ -6,7 +6,7 @@ The layer runs in hand-written HIP kernels behind the C ABI of include/moe.h
 """
 from .binding import (MoEError, alloc_routing, alloc_workspace, config_from_spec, load, make_config,  # noqa: F401
                       make_routing, make_weights, moe_capacity, moe_combine, moe_expert_ffn, moe_forward,
-                      moe_kernel_names, moe_last_error, moe_permute, moe_route, moe_route_from_logits,
+                      moe_kernel_names, moe_last_error, moe_permute, moe_permute_noalloc, moe_route, moe_route_from_logits,
                       moe_route_noisy, moe_router_losses, STAGE_LOSSES,
                       moe_timing_enable, moe_timing_read, moe_timing_reset, moe_workspace_size,
                       STAGE_FORWARD, STAGE_PERMUTE, STAGE_FFN)

@@ -20,7 +20,7 @@ DTYPE = {"f32": 0, "bf16": 1}
 STAGE_FORWARD, STAGE_PERMUTE, STAGE_FFN, STAGE_LOSSES = 0, 1, 2, 3
 
 EXPORTS = ["moe_capacity", "moe_workspace_size", "moe_route", "moe_route_noisy", "moe_route_from_logits",
-           "moe_router_losses", "moe_permute",
+           "moe_router_losses", "moe_permute", "moe_permute_noalloc",
            "moe_expert_ffn", "moe_combine", "moe_forward", "moe_last_error", "moe_timing_enable",
            "moe_timing_reset", "moe_timing_read", "moe_kernel_name"]
 
@@ -71,6 +71,7 @@ def load():
         "moe_route_noisy": [cfgp, P, ctypes.POINTER(moe_weights), P, P, ctypes.POINTER(moe_routing), P],
         "moe_router_losses": [cfgp, P, P, P, P, SZ, P],
         "moe_permute": [cfgp, P, ctypes.POINTER(moe_routing), P, P, SZ, P],
+        "moe_permute_noalloc": [cfgp, P, ctypes.POINTER(moe_routing), P, P],
         "moe_expert_ffn": [cfgp, P, P, ctypes.POINTER(moe_routing), ctypes.POINTER(moe_weights), P, P, P, SZ, P],
         "moe_combine": [cfgp, P, P, ctypes.POINTER(moe_routing), P, P],
         "moe_forward": [cfgp, P, ctypes.POINTER(moe_weights), P, ctypes.POINTER(moe_routing), P, SZ, P],
@@ -176,6 +177,11 @@ def moe_permute(cfg, x, routing: moe_routing, x_perm, ws, stream=None):
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(load().moe_permute(ctypes.byref(cfg), _p(x), ctypes.byref(routing), _p(x_perm), _p(ws), nbytes,
                               _stream(stream)))
+
+
+def moe_permute_noalloc(cfg, x, routing: moe_routing, x_perm, stream=None):
+    _check(load().moe_permute_noalloc(ctypes.byref(cfg), _p(x), ctypes.byref(routing), _p(x_perm),
+                                      _stream(stream)))
 
 
 def moe_expert_ffn(cfg, x_perm, x, routing: moe_routing, weights: moe_weights, y_perm, y_shared, ws, stream=None):

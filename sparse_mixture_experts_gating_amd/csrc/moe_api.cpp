@@ -64,11 +64,15 @@ hipEvent_t take_event() {
     return e;
 }
 
+// Launches of the allocation-free entry points record no events (creating
+// one allocates); set for the duration of such a call on this thread.
+thread_local bool t_untimed = false;
+
 // Runs one launch; with timing on, brackets it with events on its stream.
 template <class F>
 moe_status launch(int kind, hipStream_t s, F &&f) {
     hipEvent_t a = nullptr, b = nullptr;
-    if (g_timing.load(std::memory_order_relaxed)) {
+    if (!t_untimed && g_timing.load(std::memory_order_relaxed)) {
         std::lock_guard<std::mutex> lk(g_tmu);
         a = take_event();
         b = take_event();
@@ -447,6 +451,41 @@ moe_status check_routing(const Derived &D, const moe_routing *r, bool need_perm)
     return MOE_OK;
 }
 
+// ---------------------------------------------------------------------------
+// fixed scratch of the allocation-free permutation
+// ---------------------------------------------------------------------------
+// Device memory of the library itself, one copy per GPU, held until the
+// process ends.  On the host, `scratch` names only a stand-in for the device
+// array: kernels receive the device address that hipGetSymbolAddress returns
+// for the current device, never the name.
+constexpr size_t kNoAllocScratchBytes = (size_t)MOE_PERMUTE_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_dev[kMaxScratchDevices];  // device address per device, null until first use
+
+// The current device's copy of `scratch`, looked up once per device.
+moe_status scratch_of_current_device(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxScratchDevices)
+        return fail(MOE_ERR_UNSUPPORTED, "device %d: the fixed scratch is kept for devices 0..%d", dev,
+                    kMaxScratchDevices - 1);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d failed: %s", dev,
+                        hipGetErrorString(e));
+        g_scratch_dev[dev] = p;
+    }
+    *out = g_scratch_dev[dev];
+    return MOE_OK;
+}
+
 moe_status check_route_limits(const Derived &D) {
     if (D.E > 256) return fail(MOE_ERR_UNSUPPORTED, "the fused router handles at most 256 experts");
     return MOE_OK;
@@ -576,6 +615,30 @@ moe_status moe_permute(const moe_config *cfg, const void *x, moe_routing *routin
             return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, c.off);
     }
     return do_permute(D, x, routing, x_perm, (char *)ws, pw, (hipStream_t)stream);
+}
+
+moe_status moe_permute_noalloc(const moe_config *cfg, const void *x, moe_routing *routing, void *x_perm,
+                               void *stream) {
+    g_err.clear();
+    Derived D;
+    TRY(derive(cfg, &D));
+    if (D.T == 0) return MOE_OK;  // empty batch: nothing to launch
+    TRY(check_routing(D, routing, true));
+    TRY(need_ptr(x, "x"));
+    TRY(need_ptr(x_perm, "x_perm"));
+    Carve c;
+    const PermuteWs pw = carve_permute(D, c);
+    if (c.off > kNoAllocScratchBytes)
+        return fail(MOE_ERR_UNSUPPORTED, "permutation scratch of %zu bytes exceeds the fixed %zu bytes", c.off,
+                    kNoAllocScratchBytes);
+    void *ws = nullptr;
+    TRY(scratch_of_current_device(&ws));
+    // every scratch entry the kernels read is written earlier in this call,
+    // so nothing is cleared between calls
+    t_untimed = true;
+    const moe_status st = do_permute(D, x, routing, x_perm, (char *)ws, pw, (hipStream_t)stream);
+    t_untimed = false;
+    return st;
 }
 
 moe_status moe_expert_ffn(const moe_config *cfg, const void *x_perm, const void *x, const moe_routing *routing,

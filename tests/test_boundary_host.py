@@ -114,3 +114,20 @@ def test_empty_batch_is_a_no_op():
     cfg = moe.config_from_spec(workloads.MIXTRAL_PREFILL_BF16.replace(T=0))
     lib = moe.load()
     assert lib.moe_forward(ctypes.byref(cfg), None, None, None, None, None, 0, None) == 0
+
+
+def test_permute_noalloc_rejects_before_any_device_call():
+    """The allocation-free permutation refuses, on the host, a batch whose
+    scratch exceeds its fixed array, and null routing buffers."""
+    lib = moe.load()
+    spec = workloads.DEEPSEEK_SHARED_BF16.replace(T=200000)
+    cfg = moe.config_from_spec(spec)
+    assert moe.moe_workspace_size(cfg, moe.STAGE_PERMUTE) > (8 << 20)
+    r = binding.moe_routing(*([ctypes.c_void_p(256)] * 7))
+    p = ctypes.c_void_p(256)
+    assert lib.moe_permute_noalloc(ctypes.byref(cfg), p, ctypes.byref(r), p, None) == 2
+    assert b"exceeds the fixed" in lib.moe_last_error()
+    ok = moe.config_from_spec(workloads.DEEPSEEK_SHARED_BF16)
+    assert moe.moe_workspace_size(ok, moe.STAGE_PERMUTE) <= (8 << 20)
+    assert lib.moe_permute_noalloc(ctypes.byref(ok), p, None, p, None) == 1
+    assert lib.moe_permute_noalloc(ctypes.byref(ok), None, ctypes.byref(r), p, None) == 1
