@@ -35,7 +35,7 @@ def active_flops(spec, counts):
     mult = 3 if spec.act == "swiglu" else 2
     router = 2.0 * spec.T * spec.d * spec.E
     experts = 2.0 * float(sum(counts)) * spec.d * spec.F * mult
-    shared = 2.0 * spec.T * spec.d * spec.F_shared * 3 if spec.F_shared else 0.0
+    shared = 2.0 * spec.T * spec.d * spec.F_shared * 3 * spec.num_shared if spec.F_shared else 0.0
     return router + experts + shared
 
 
@@ -45,7 +45,7 @@ def kernel_work(spec, counts, name):
     every expert that received rows once, each intermediate written and read
     once, routing metadata); re-reads caused by tiling are not counted."""
     eb = 2 if spec.dtype == "bf16" else 4
-    T, d, E, F, Fs = spec.T, spec.d, spec.E, spec.F, spec.F_shared
+    T, d, E, F, Fs = spec.T, spec.d, spec.E, spec.F, spec.F_shared * spec.num_shared  # shared: S stacked experts
     ec = spec.gating == "expert_choice"
     rows = float(sum(counts))                      # kept (routed) rows
     touched = sum(1 for c in counts if c > 0)      # experts that received rows
@@ -307,7 +307,8 @@ def main():
         "dtype": spec.dtype,
         "data": "synthetic (seeded Gaussian tokens, N(0,1/fan_in) weights)",
         "config": {"workload": spec.name, "tokens": spec.T, "d_model": spec.d, "experts": spec.E,
-                   "top_k": spec.k, "d_ff": spec.F, "d_ff_shared": spec.F_shared, "gating": spec.gating,
+                   "top_k": spec.k, "d_ff": spec.F, "d_ff_shared": spec.F_shared,
+                   "num_shared": spec.num_shared if spec.F_shared else 0, "gating": spec.gating,
                    "activation": spec.act, "parallelism": "none (1 GPU)"},
         "layer_tflops_active": round(layer_tflops, 2),
         "layer_frac_bf16_peak": round(layer_tflops / PEAK_BF16_TFLOPS, 4),

@@ -32,6 +32,8 @@
  *     accumulation; MOE_F32 is float32 throughout.
  *   - Supported shapes (else MOE_ERR_UNSUPPORTED): d_model, d_ff and
  *     d_ff_shared multiples of 64 (bf16) or 16 (f32) and at most 2^21;
+ *     num_shared * d_ff_shared at most 2^21 and the shared down projection
+ *     (num_shared * d_model * d_ff_shared elements) under 2^31 bytes;
  *     num_experts <= 1024, and <= 256 for the fused router and the router
  *     losses; expert-choice capacity <= 4096; T * k < 2^31.
  */
@@ -79,7 +81,11 @@ typedef enum moe_gating {
  *   MOE_ACT_GELU_ERF  y = W2 gelu(W1 u + b1) + b2, exact erf GELU ([yj-zh] MoELayer)
  *   MOE_ACT_SWIGLU    y = W2 (silu(W1 u) * (W3 u)) ([yj-zh] SwiGLUExpert w1/w3/w2;
  *                     [yj-ja] SwiGLUExpert w_gate/w_up/w_down; [lecture] SwiGLU row)
- * The optional shared expert is always SwiGLU ([yj-zh] DeepSeekMoELayer). */
+ * The optional shared experts are always SwiGLU ([yj-zh] DeepSeekMoELayer).
+ * S of them of width Fs run as one SwiGLU expert of width S*Fs: their
+ * stacked gate and up rows are the [S*Fs][d] matrices of that expert, and the
+ * down projection reads the S [d][Fs] blocks as consecutive slices of its
+ * hidden axis, so the S outputs are summed inside one accumulation. */
 typedef enum moe_act { MOE_ACT_RELU = 0, MOE_ACT_GELU_ERF = 1, MOE_ACT_SWIGLU = 2 } moe_act;
 
 typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
@@ -90,7 +96,7 @@ typedef struct moe_config {
     int32_t num_experts;     /* E, routed experts */
     int32_t top_k;           /* k, token choice only */
     int32_t d_ff;            /* F, hidden width of each routed expert */
-    int32_t d_ff_shared;     /* hidden width of one always-on shared expert, 0 = none */
+    int32_t d_ff_shared;     /* hidden width Fs of each always-on shared expert, 0 = none */
     int32_t gating;          /* moe_gating */
     int32_t act;             /* moe_act */
     int32_t dtype;           /* moe_dtype of x, all weights, x_perm, y_perm and y */
@@ -106,6 +112,11 @@ typedef struct moe_config {
                                 dropped.  EXPERT_CHOICE: C = int(cf * T / E). */
     int32_t min_capacity;    /* floor of the token-choice capacity ([yj-zh]
                                 DeepSpeed MoE configuration example); 0 = none */
+    int32_t num_shared;      /* S always-on shared SwiGLU experts of width
+                                d_ff_shared, whose outputs are summed ([yj-zh]
+                                DeepSeekMoELayer num_shared_experts; [devtips]
+                                DeepSeekMoE); must be >= 1 when d_ff_shared > 0
+                                and is ignored when d_ff_shared == 0 */
 } moe_config;
 
 /* Weights (device pointers). */
@@ -117,9 +128,9 @@ typedef struct moe_weights {
     const void *w2;        /* [E][d][F] down projection */
     const float *b1;       /* [E][F] float32 or NULL; ReLU/GELU only */
     const float *b2;       /* [E][d] float32 or NULL; ReLU/GELU only */
-    const void *ws1;       /* shared expert gate  [Fs][d] dtype, or NULL */
-    const void *ws3;       /* shared expert up    [Fs][d] dtype, or NULL */
-    const void *ws2;       /* shared expert down  [d][Fs] dtype, or NULL */
+    const void *ws1;       /* shared experts' gate  [S][Fs][d] dtype, or NULL */
+    const void *ws3;       /* shared experts' up    [S][Fs][d] dtype, or NULL */
+    const void *ws2;       /* shared experts' down  [S][d][Fs] dtype, or NULL */
 } moe_weights;
 
 /* Routing buffers (device pointers), written by moe_route / moe_permute and
@@ -217,8 +228,8 @@ moe_status moe_permute_noalloc(const moe_config *cfg, const void *x, moe_routing
                                void *stream);
 
 /* Expert FFNs as grouped GEMMs over the expert-contiguous rows: y_perm [A_max][d]
- * (dtype) for rows < offsets[E]; y_shared [T][d] (dtype) = shared expert of x
- * when cfg->d_ff_shared > 0 (x: device [T][d], else may be NULL).  Only the
+ * (dtype) for rows < offsets[E]; y_shared [T][d] (dtype) = the sum of the
+ * shared experts of x when cfg->d_ff_shared > 0 (x: device [T][d], else may be NULL).  Only the
  * rows routed to an expert are computed for it ([lecture] "Token Routing":
  * unselected experts do no work).  ws: MOE_STAGE_FFN bytes (holds the hidden
  * activations). */

@@ -283,10 +283,24 @@ def _experts_rows(spec, inp, X, expert_of_row):
     return Y
 
 
+def shared_ffn(X, ws1, ws3, ws2) -> np.ndarray:
+    """Always-on shared SwiGLU experts on rows X -> float64 [n, d]: one expert
+    (ws1, ws3 [Fs, d], ws2 [d, Fs]) or the sum of S of them (ws1, ws3
+    [S, Fs, d], ws2 [S, d, Fs]), added in expert order ([yj-zh]
+    DeepSeekMoELayer sums its shared experts; [devtips] DeepSeekMoE)."""
+    ws1, ws3, ws2 = _f32(ws1), _f32(ws3), _f32(ws2)
+    if ws1.ndim == 2:
+        return expert_ffn("swiglu", X, ws1, ws3, ws2)
+    out = expert_ffn("swiglu", X, ws1[0], ws3[0], ws2[0])
+    for s in range(1, ws1.shape[0]):
+        out = out + expert_ffn("swiglu", X, ws1[s], ws3[s], ws2[s])
+    return out
+
+
 def _shared(spec, inp, X):
     if not spec.F_shared:
         return None
-    return expert_ffn("swiglu", X, inp["ws1"], inp["ws3"], inp["ws2"])
+    return shared_ffn(X, inp["ws1"], inp["ws3"], inp["ws2"])
 
 
 def forward(spec, inp, lg=None) -> dict:
@@ -391,7 +405,7 @@ def forward_tokens(spec, inp, tokens, lg=None) -> dict:
         for r, (i, g) in enumerate(mine):
             y[i] += g * Ye[r]
     if spec.F_shared:
-        y += expert_ffn("swiglu", xs, _f32(inp["ws1"]), _f32(inp["ws3"]), _f32(inp["ws2"]))
+        y += shared_ffn(xs, inp["ws1"], inp["ws3"], inp["ws2"])
     res["y"] = y.astype(np.float32)
     res["y64"] = y
     return res

@@ -36,7 +36,7 @@ class moe_config(ctypes.Structure):
                 ("top_k", ctypes.c_int32), ("d_ff", ctypes.c_int32), ("d_ff_shared", ctypes.c_int32),
                 ("gating", ctypes.c_int32), ("act", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("capacity_group", ctypes.c_int32), ("capacity_factor", ctypes.c_float),
-                ("min_capacity", ctypes.c_int32)]
+                ("min_capacity", ctypes.c_int32), ("num_shared", ctypes.c_int32)]
 
 
 class moe_weights(ctypes.Structure):
@@ -112,16 +112,17 @@ def _stream(stream):
 # ---------------------------------------------------------------------------
 
 def make_config(T, d, E, k, F, gating, act, dtype, F_shared=0, capacity_factor=0.0, capacity_group=0,
-                min_capacity=0):
+                min_capacity=0, num_shared=1):
     return moe_config(T, d, E, k, F, F_shared, GATING[gating], ACT[act], DTYPE[dtype], capacity_group,
-                      float(capacity_factor), int(min_capacity))
+                      float(capacity_factor), int(min_capacity), int(num_shared) if F_shared else 0)
 
 
 def config_from_spec(spec) -> moe_config:
     """moe_config of a layer description with attributes T, d, E, k, F, gating, act, dtype,
-    F_shared, capacity_factor, capacity_group."""
+    F_shared, capacity_factor, capacity_group (and optionally min_capacity, num_shared)."""
     return make_config(spec.T, spec.d, spec.E, spec.k, spec.F, spec.gating, spec.act, spec.dtype,
-                       spec.F_shared, spec.capacity_factor, spec.capacity_group, getattr(spec, "min_capacity", 0))
+                       spec.F_shared, spec.capacity_factor, spec.capacity_group, getattr(spec, "min_capacity", 0),
+                       getattr(spec, "num_shared", 1))
 
 
 def make_weights(t: dict) -> moe_weights:

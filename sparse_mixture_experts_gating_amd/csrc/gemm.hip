@@ -125,6 +125,9 @@ struct GemmParams {
     // a_bytes bytes one buffer resource covers (null: rows in place)
     const int32_t *arow;
     int64_t a_bytes;
+    // K-sliced B (one group): K = (K / kslice) slices of kslice, slice s a
+    // [N][kslice] matrix at B0 + s * N * kslice; 0 = B is [N][K]
+    int kslice;
 };
 
 // Work item of one workgroup.  The tiles fill rounds of `slots` workgroups;
@@ -205,8 +208,10 @@ __device__ inline void dispatch_active(int n, F &&f) {
 // instead of the same one.  JOUT: MFMA order with the B fragment in the outer
 // loop (each B fragment feeds NA MFMAs in a row, the A fragments change every
 // MFMA) instead of the A fragment.
+// SL: B is K-sliced (p.kslice > 0): the rows of each K tile are read from
+// its slice (the shared experts' down projections side by side along K).
 template <int BM, int BN, int WM, int WN, bool GLU, int IL = 0, int MF = 32, bool RMAP = false, int BK = 64,
-          bool JOUT = false>
+          bool JOUT = false, bool SL = false>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
     constexpr int NT = 64 * WM * WN;  // threads
     static_assert(BK == 64 || BK == 128, "K tile");
@@ -265,13 +270,28 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
     const int64_t k0 = (int64_t)kbeg * BK;
     // Gathered A: one resource over all of A and a per-row byte offset from
     // the row map; padding rows get an offset past the limit (zeros).
+    static_assert(!(SL && GLU), "K-sliced B is for the down projection");
     const char *abase = p.arow ? (const char *)(p.A + k0) : (const char *)(p.A + tc.row0 * K + k0);
-    const char *b0base = (const char *)(p.B0 + ((int64_t)tc.g * p.N + n0) * K + k0);
+    // B row stride: K, or the slice width (then every K offset, k0 included,
+    // goes into the per-tile scalar offset)
+    const int64_t bstride = SL ? p.kslice : K;
+    const char *b0base = SL ? (const char *)(p.B0 + (int64_t)n0 * bstride)
+                            : (const char *)(p.B0 + ((int64_t)tc.g * p.N + n0) * K + k0);
     const char *b1base = GLU ? (const char *)(p.B1 + ((int64_t)tc.g * p.N + n0) * K + k0) : nullptr;
     const __amdgpu_buffer_rsrc_t arsrc =
         buffer_rsrc(abase, p.arow ? p.a_bytes - k0 * 2 : (tc.row_end - tc.row0) * K * 2);
-    const __amdgpu_buffer_rsrc_t b0rsrc = buffer_rsrc(b0base, (int64_t)(p.N - n0) * K * 2);
+    const __amdgpu_buffer_rsrc_t b0rsrc =
+        buffer_rsrc(b0base, SL ? ((K / bstride) * p.N - n0) * bstride * 2 : (int64_t)(p.N - n0) * K * 2);
     const __amdgpu_buffer_rsrc_t b1rsrc = GLU ? buffer_rsrc(b1base, (int64_t)(p.N - n0) * K * 2) : b0rsrc;
+    // byte offset of K tile kt (of this work item) inside B: its slice, then its column
+    auto bk_off = [&](int kt) {
+        if constexpr (SL) {
+            const int64_t kk = (int64_t)(kbeg + kt) * BK;
+            return (int)((kk / bstride) * p.N * bstride * 2 + (kk % bstride) * 2);
+        } else {
+            return kt * BK * 2;
+        }
+    };
     uint32_t aoff[A_PER_T], boff[B_PER_T];
 #pragma unroll
     for (int i = 0; i < A_PER_T; ++i) {
@@ -283,7 +303,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
     for (int i = 0; i < B_PER_T; ++i) {
         int r = r0 + RSTEP * i;
         if (GLU && r >= BN) r -= BN;
-        boff[i] = (uint32_t)(((int64_t)r * K + ch0 * 8) * 2);
+        boff[i] = (uint32_t)(((int64_t)r * bstride + ch0 * 8) * 2);
     }
     // LDS: chunk c of row r sits at chunk slot c ^ swz(r); swz is the same for
     // all of a thread's rows (they differ by multiples of 16), so one base
@@ -308,13 +328,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
     // MFMAs consume one, the next tile is stored into the other.
     u32x4 ra[2][A_PER_T], rb[2][B_PER_T];
     auto gload = [&](int kt, int set) {
-        const int ko = kt * BK * 2;
+        const int ko = kt * BK * 2, kob = bk_off(kt);
 #pragma unroll
         for (int i = 0; i < A_PER_T; ++i) ra[set][i] = buffer_load16(arsrc, aoff[i], ko);
 #pragma unroll
         for (int i = 0; i < B_PER_T; ++i) {
             const bool up = GLU && RSTEP * i >= BN;
-            rb[set][i] = buffer_load16(up ? b1rsrc : b0rsrc, boff[i], ko);
+            rb[set][i] = buffer_load16(up ? b1rsrc : b0rsrc, boff[i], kob);
         }
     };
     auto lstore = [&](int buf, int set) {
@@ -540,6 +560,7 @@ struct GemmParamsF32 {
     int64_t rows;
     int N, K;
     int act;
+    int kslice;  // K-sliced B as in GemmParams; 0 = B is [N][K]
 };
 
 constexpr int kF32BM = 32;
@@ -578,19 +599,22 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParamsF32 p) {
         int n = n0 + r;
         if (n >= p.N) n = p.N - 1;
 #pragma unroll
-        for (int u = 0; u < NU; ++u) brow[u][i] = Bg[u] + (int64_t)n * K;
+        for (int u = 0; u < NU; ++u) brow[u][i] = Bg[u] + (int64_t)n * (p.kslice ? p.kslice : K);
     }
     const int kq = 4 * (tid % 16);
     float4 ra[2], rb[NU][2];
     auto gload = [&](int k0) {
         const int k = k0 + kq;
         const bool in = k < p.K;  // K is a multiple of 16: a float4 is all in or all out
+        // K-sliced B (the shared experts' down projections): column k is
+        // column k % kslice of slice k / kslice; a float4 stays in one slice
+        const int64_t bk = p.kslice ? (int64_t)(k / p.kslice) * p.N * p.kslice + k % p.kslice : k;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             ra[i] = in ? *(const float4 *)(arow[i] + k) : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
             for (int u = 0; u < NU; ++u)
-                rb[u][i] = in ? *(const float4 *)(brow[u][i] + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+                rb[u][i] = in ? *(const float4 *)(brow[u][i] + bk) : make_float4(0.f, 0.f, 0.f, 0.f);
         }
     };
     auto lstore = [&]() {
@@ -704,14 +728,14 @@ static int64_t grid_for(const GemmArgs &a, int BM, int BN) {
 }
 
 template <int BM, int BN, int WM, int WN, bool GLU, int MF = 16, bool RMAP = false, int IL = 0, int BK = 64,
-          bool JOUT = false>
+          bool JOUT = false, bool SL = false>
 static void launch_bf16_t(const GemmArgs &a, hipStream_t s) {
     constexpr int NB = GLU ? 2 * BN : BN;
     static_assert((int64_t)BM * NB <= kSplitUnitFloats, "split-K unit");
-    auto kern = gemm_bf16_kernel<BM, BN, WM, WN, GLU, IL, MF, RMAP, BK, JOUT>;
+    auto kern = gemm_bf16_kernel<BM, BN, WM, WN, GLU, IL, MF, RMAP, BK, JOUT, SL>;
     GemmParams p{(const bf16 *)a.A, (const bf16 *)a.B0, (const bf16 *)a.B1, a.bias, (bf16 *)a.C,
                  a.offsets, a.mstart, a.mtile, a.max_mt, a.G, a.rows, a.N, a.K, a.act, nullptr, nullptr, 0, 1, 0,
-                 a.arow, a.a_rows * a.K * 2};
+                 a.arow, a.a_rows * a.K * 2, SL ? a.kslice : 0};
     int64_t grid = grid_for(a, BM, BN);
     if (grid == 0) return;
     // Split K of the last round needs the number of co-resident workgroups
@@ -749,7 +773,7 @@ static void launch_bf16_t(const GemmArgs &a, hipStream_t s) {
 template <bool GLU>
 static void launch_f32_t(const GemmArgs &a, hipStream_t s) {
     GemmParamsF32 p{(const float *)a.A, (const float *)a.B0, (const float *)a.B1, a.bias, (float *)a.C,
-                    a.offsets, a.mstart, a.mtile, a.max_mt, a.G, a.rows, a.N, a.K, a.act};
+                    a.offsets, a.mstart, a.mtile, a.max_mt, a.G, a.rows, a.N, a.K, a.act, a.kslice};
     const int64_t grid = grid_for(a, kF32BM, 32);
     if (grid == 0) return;
     hipLaunchKernelGGL((gemm_f32_kernel<GLU>), dim3((unsigned)grid), dim3(256), 0, s, p);
@@ -781,6 +805,13 @@ void launch_grouped_gemm(const GemmArgs &a, int shape, hipStream_t s) {
     // 32-tile XCD group.  Balanced tiles of one group are equally long, and
     // the split rows (RMAP) give each SIMD one wave of each row half, so the
     // skipped blocks shorten every SIMD's work alike.
+    if (a.kslice > 0) {
+        // K-sliced B: the shared experts' down projection (one group, decode
+        // or prefill tiles, same schedules as below)
+        if (shape == kGemmDecode) launch_bf16_t<32, 128, 1, 4, false, 32, false, 0, 64, false, true>(a, s);
+        else launch_bf16_t<256, 256, 2, 4, false, 16, true, 1, 64, false, true>(a, s);
+        return;
+    }
     if (shape == kGemmDecode) {
         // gate/up: K tiles of 128 (256 bytes of each weight row per load
         // round rather than 128: a plain read of the decode tile's weight

@@ -132,6 +132,10 @@ struct GemmArgs {
     // loads themselves).  Needs a_rows * K * 2 < 2^31.
     const int32_t *arow = nullptr;
     int64_t a_rows = 0;
+    // K-sliced B (one group, not SwiGLU): B holds K / kslice matrices
+    // [N][kslice] one after another, slice s supplying columns s * kslice ..
+    // (s+1) * kslice - 1 of the K axis; 0 = B is [G][N][K].
+    int kslice = 0;
 };
 enum GemmShape { kGemmPrefill = 0, kGemmSmallM = 1, kGemmDecode = 2 };
 int gemm_block_m(int shape, bool bf16);

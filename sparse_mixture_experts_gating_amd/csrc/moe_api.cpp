@@ -99,6 +99,7 @@ moe_status launch(int kind, hipStream_t s, F &&f) {
 // ---------------------------------------------------------------------------
 struct Derived {
     int64_t T, d, E, k, F, Fs;
+    int64_t Ns, Fsum;  // shared experts and their stacked hidden width Ns * Fs
     int gating, act;
     bool bf16, ec;
     int capacity;      // Switch / expert choice, else 0
@@ -139,6 +140,10 @@ moe_status derive(const moe_config *c, Derived *o) {
     o->E = c->num_experts;
     o->F = c->d_ff;
     o->Fs = c->d_ff_shared;
+    o->Ns = o->Fs > 0 ? c->num_shared : 0;
+    if (o->Fs > 0 && c->num_shared < 1)
+        return fail(MOE_ERR_INVALID_ARG, "num_shared must be >= 1 when d_ff_shared > 0");
+    o->Fsum = o->Ns * o->Fs;
     o->gating = c->gating;
     o->act = c->act;
     o->bf16 = c->dtype == MOE_BF16;
@@ -175,8 +180,11 @@ moe_status derive(const moe_config *c, Derived *o) {
     if (o->d % kq || o->F % kq || o->Fs % kq)
         return fail(MOE_ERR_UNSUPPORTED, "d_model, d_ff and d_ff_shared must be multiples of %d for this dtype", kq);
     // the GEMM tiles address up to 256 rows from a tile base with 32-bit byte offsets
-    if (std::max(std::max(o->d, o->F), o->Fs) > (1 << 21))
-        return fail(MOE_ERR_UNSUPPORTED, "d_model, d_ff and d_ff_shared must be at most %d", 1 << 21);
+    if (std::max(std::max(o->d, o->F), o->Fsum) > (1 << 21))
+        return fail(MOE_ERR_UNSUPPORTED, "d_model, d_ff and num_shared * d_ff_shared must be at most %d", 1 << 21);
+    // the shared experts' down projections are read through one buffer resource
+    if (o->Ns > 1 && o->Fsum * o->d * (int64_t)o->elem > 0x7fffffff)
+        return fail(MOE_ERR_UNSUPPORTED, "the shared down projections exceed 2^31 bytes");
     o->slots = o->ec ? o->E * o->capacity : o->T * o->k;
     o->a_max = o->slots;
     o->S = o->ec ? o->E : o->k;
@@ -237,7 +245,7 @@ FfnWs carve_ffn(const Derived &D, Carve &c) {
     w.max_mt = (int)max_mtiles(D.a_max, (int)D.E);
     w.mtile = c.take((size_t)w.max_mt * 16);
     w.h = c.take((size_t)D.a_max * D.F * D.elem);
-    w.hs = D.Fs ? c.take((size_t)D.T * D.Fs * D.elem) : 0;
+    w.hs = D.Fs ? c.take((size_t)D.T * D.Fsum * D.elem) : 0;
     if (D.bf16) {
         // split-K partial tiles: one largest tile per CU (the bf16 shapes with
         // several workgroups per CU have proportionally smaller tiles)
@@ -419,13 +427,18 @@ moe_status do_ffn(const Derived &D, const void *x_perm, const void *x, const moe
                 (int)D.F, kActNone, D.bf16, split};
     TRY(launch(K_GEMM2, s, [&] { launch_grouped_gemm(g2, shape, s); }));
     if (D.Fs) {
+        // The Ns shared experts as one SwiGLU expert of width Ns * Fs: their
+        // stacked [Ns][Fs][d] gate and up weights are its [Ns*Fs][d] rows, and
+        // the down projection takes its K axis from the Ns [d][Fs] blocks in
+        // turn (K-sliced B), so the experts' outputs add up in one accumulation.
         const int sshape = D.T <= 32 ? kGemmDecode : kGemmPrefill;
         void *Hs = ws + fw.hs;
-        GemmArgs s1{x, w->ws1, w->ws3, nullptr, Hs, nullptr, nullptr, nullptr, 0, 1, D.T, (int)D.Fs, (int)D.d,
+        GemmArgs s1{x, w->ws1, w->ws3, nullptr, Hs, nullptr, nullptr, nullptr, 0, 1, D.T, (int)D.Fsum, (int)D.d,
                     kActSwiglu, D.bf16, split};
         TRY(launch(K_GEMM1_SHARED, s, [&] { launch_grouped_gemm(s1, sshape, s); }));
         GemmArgs s2{Hs, w->ws2, nullptr, nullptr, y_shared, nullptr, nullptr, nullptr, 0, 1, D.T, (int)D.d,
-                    (int)D.Fs, kActNone, D.bf16, split};
+                    (int)D.Fsum, kActNone, D.bf16, split};
+        if (D.Ns > 1) s2.kslice = (int)D.Fs;
         TRY(launch(K_GEMM2_SHARED, s, [&] { launch_grouped_gemm(s2, sshape, s); }));
     }
     return MOE_OK;

@@ -245,6 +245,16 @@ ABI_SPECS = [
     workloads.DEEPSEEK_SHARED_BF16.replace(name="shared_expert_f32", dtype="f32", T=200, d=128, E=32, k=4, F=64,
                                            F_shared=96),
     workloads.EXPERT_CHOICE_BF16.replace(name="expert_choice_f32", dtype="f32", T=500, d=128, E=8, F=96),
+    # several shared experts, summed ([yj-zh] DeepSeekMoELayer): the down
+    # projection reads their [S][d][Fs] blocks as slices of its K axis
+    workloads.DEEPSEEK_SHARED_BF16.replace(name="two_shared_experts", T=520, d=384, E=64, F=256, F_shared=320,
+                                           num_shared=2),
+    workloads.DEEPSEEK_SHARED_BF16.replace(name="three_shared_experts_decode", T=16, d=512, E=16, k=4, F=128,
+                                           F_shared=192, num_shared=3),
+    workloads.DEEPSEEK_SHARED_BF16.replace(name="two_shared_experts_f32", dtype="f32", T=200, d=128, E=32, k=4,
+                                           F=64, F_shared=96, num_shared=2),
+    workloads.DEEPSEEK_SHARED_BF16.replace(name="two_shared_experts_split_k", T=520, d=512, E=64, F=64,
+                                           F_shared=2048, num_shared=2),
 ]
 FFN_SPECS = FFN_SPECS + LONG_K_SPECS + SPLITK_SPECS + ABI_SPECS
 
@@ -296,7 +306,7 @@ def _check_ffn(spec, inp, dinp, counts, row_token):
         assert rel_err(got[rows], ref) <= TOL[spec.dtype], f"expert {e}"
     assert (got[n:] == 3.0).all()  # rows past the routed ones are untouched
     if spec.F_shared:
-        ref = oracle.expert_ffn("swiglu", inp["x"], inp["ws1"], inp["ws3"], inp["ws2"])
+        ref = oracle.shared_ffn(inp["x"], inp["ws1"], inp["ws3"], inp["ws2"])
         assert rel_err(_np(y_shared), ref) <= TOL[spec.dtype]
 
 

@@ -55,6 +55,13 @@ def _np_inputs(spec, inp):
     return {k: (None if v is None else v.float().numpy()) for k, v in inp.items()}
 
 
+def _ref_shared(x, ws1, ws3, ws2):
+    """Shared experts via float64 numpy: one (2-D weights) or the sum of S ([S, ...] weights)."""
+    if ws1.ndim == 2:
+        return _ref_expert("swiglu", x, ws1, ws3, ws2)
+    return sum(_ref_expert("swiglu", x, ws1[s], ws3[s], ws2[s]) for s in range(ws1.shape[0]))
+
+
 # ---------------------------------------------------------------------------
 # logits
 # ---------------------------------------------------------------------------
@@ -312,7 +319,7 @@ def _dense_mixture(spec, inp, G):
                          None if inp["b2"] is None else inp["b2"][e])
         y += G[:, e:e + 1] * Ye
     if spec.F_shared:
-        y += _ref_expert("swiglu", x, inp["ws1"], inp["ws3"], inp["ws2"])
+        y += _ref_shared(x, inp["ws1"], inp["ws3"], inp["ws2"])
     return y
 
 
@@ -326,6 +333,8 @@ TINY = [
     workloads.EXPERT_CHOICE_BF16.replace(name="tiny_ec", T=64, d=32, E=8, F=24),
     workloads.MIXTRAL_PREFILL_BF16.replace(name="tiny_softmax_topk", T=30, d=16, F=24,
                                            gating="softmax_topk"),
+    workloads.DEEPSEEK_SHARED_BF16.replace(name="tiny_deepseek_3_shared", T=40, d=32, E=16, k=4, F=16,
+                                           F_shared=24, num_shared=3),
 ]
 
 
@@ -373,7 +382,7 @@ def test_identical_experts_closed_form(spec):
                       None if npi["b2"] is None else npi["b2"][0])
     shared = 0.0
     if spec.F_shared:
-        shared = _ref_expert("swiglu", npi["x"], npi["ws1"], npi["ws3"], npi["ws2"])
+        shared = _ref_shared(npi["x"], npi["ws1"], npi["ws3"], npi["ws2"])
     if spec.gating == "topk_softmax":
         scale = np.ones((spec.T, 1))
     elif spec.gating == "switch":
@@ -397,6 +406,35 @@ def test_single_expert_is_plain_ffn():
     assert np.allclose(out["y64"], ref, rtol=1e-12, atol=1e-12)
 
 
+def test_several_shared_experts_equal_one_wide_expert():
+    """S shared SwiGLU experts of width Fs summed ([yj-zh] DeepSeekMoELayer)
+    equal one SwiGLU expert of width S*Fs whose gate and up rows are the S
+    experts' rows stacked and whose down projection is theirs concatenated
+    along the hidden axis: the hidden units split into S groups and the
+    down projection sums over all of them."""
+    spec = workloads.DEEPSEEK_SHARED_BF16.replace(name="shared_stack", T=23, d=32, E=4, F=16, F_shared=24,
+                                                  num_shared=3)
+    npi = _np_inputs(spec, workloads.make_inputs(spec))
+    ws1, ws3, ws2 = npi["ws1"], npi["ws3"], npi["ws2"]
+    S, Fs, d = ws1.shape
+    got = oracle.shared_ffn(npi["x"], ws1, ws3, ws2)
+    wide = oracle.expert_ffn("swiglu", npi["x"], ws1.reshape(S * Fs, d), ws3.reshape(S * Fs, d),
+                             np.concatenate(list(ws2), axis=1))
+    assert np.allclose(got, wide, rtol=1e-12, atol=1e-13)
+    assert not np.allclose(got, oracle.expert_ffn("swiglu", npi["x"], ws1[0], ws3[0], ws2[0]), rtol=1e-3)
+
+
+def test_identical_shared_experts_add_up():
+    """S identical shared experts give S times one expert's output."""
+    spec = workloads.DEEPSEEK_SHARED_BF16.replace(name="shared_same", T=19, d=32, E=4, F=16, F_shared=24,
+                                                  num_shared=4)
+    npi = _np_inputs(spec, workloads.make_inputs(spec))
+    same = {k: np.broadcast_to(npi[k][:1], npi[k].shape).copy() for k in ("ws1", "ws3", "ws2")}
+    got = oracle.shared_ffn(npi["x"], same["ws1"], same["ws3"], same["ws2"])
+    one = _ref_expert("swiglu", npi["x"], npi["ws1"][0], npi["ws3"][0], npi["ws2"][0])
+    assert np.allclose(got, 4.0 * one, rtol=1e-12, atol=1e-13)
+
+
 def test_shared_expert_only_when_routed_experts_vanish():
     spec = TINY[3]
     inp = workloads.make_inputs(spec)
@@ -404,6 +442,13 @@ def test_shared_expert_only_when_routed_experts_vanish():
     out = oracle.forward(spec, inp)
     npi = _np_inputs(spec, inp)
     ref = _ref_expert("swiglu", npi["x"], npi["ws1"], npi["ws3"], npi["ws2"])
+    assert np.allclose(out["y64"], ref, rtol=1e-12, atol=1e-12)
+    spec3 = [s for s in TINY if s.num_shared == 3][0]
+    inp = workloads.make_inputs(spec3)
+    inp["w2"] = torch.zeros_like(inp["w2"])
+    out = oracle.forward(spec3, inp)
+    npi = _np_inputs(spec3, inp)
+    ref = sum(_ref_expert("swiglu", npi["x"], npi["ws1"][s], npi["ws3"][s], npi["ws2"][s]) for s in range(3))
     assert np.allclose(out["y64"], ref, rtol=1e-12, atol=1e-12)
 
 

@@ -45,7 +45,8 @@ class LayerSpec:
     dtype: str          # f32 | bf16
     expert_bias: bool = False
     router_bias: str = "none"   # none | normal | skew | zipf
-    F_shared: int = 0           # one always-on SwiGLU expert of this width; 0 = none
+    F_shared: int = 0           # width of each always-on SwiGLU shared expert; 0 = none
+    num_shared: int = 1         # shared experts (with F_shared > 0), summed
     capacity_factor: float = 0.0
     capacity_group: int = 0     # tokens per capacity group (sequence length); 0 = all tokens
     inputs: str = "gaussian"    # gaussian | integer
@@ -125,8 +126,9 @@ def make_inputs(spec: LayerSpec, device="cpu", experts: bool = True) -> dict:
 
     Returns a dict of tensors on ``device``: x [T,d], wg [E,d], bg [E] float32 or
     None, w1 [E,F,d], w3 [E,F,d] (SwiGLU) or None, w2 [E,d,F], b1 [E,F] / b2
-    [E,d] float32 or None, and ws1 [Fs,d], ws3 [Fs,d], ws2 [d,Fs] for the
-    shared expert or None.  ``experts=False`` skips the expert weights.
+    [E,d] float32 or None, and ws1 [Fs,d], ws3 [Fs,d], ws2 [d,Fs] for one
+    shared expert ([S,Fs,d], [S,Fs,d], [S,d,Fs] for S > 1 of them) or None.
+    ``experts=False`` skips the expert weights.
     """
     dt = spec.torch_dtype
     T, d, E, F = spec.T, spec.d, spec.E, spec.F
@@ -163,10 +165,14 @@ def make_inputs(spec: LayerSpec, device="cpu", experts: bool = True) -> dict:
         out["b1"] = _randn((E, F), _seed(spec, 13), device, 0.1)
         out["b2"] = _randn((E, d), _seed(spec, 14), device, 0.1)
     if spec.F_shared:
-        Fs = spec.F_shared
-        out["ws1"] = _randn((Fs, d), _seed(spec, 20), device, 1.0 / math.sqrt(d)).to(dt)
-        out["ws3"] = _randn((Fs, d), _seed(spec, 21), device, 1.0 / math.sqrt(d)).to(dt)
-        out["ws2"] = _randn((d, Fs), _seed(spec, 22), device, 1.0 / math.sqrt(Fs)).to(dt)
+        Fs, S = spec.F_shared, spec.num_shared
+        # shared expert s is seeded like routed expert s; one expert keeps 2-D tensors
+        def stack(tensor_id, shape, std):
+            parts = [_randn(shape, _seed(spec, tensor_id, s), device, std).to(dt) for s in range(S)]
+            return parts[0] if S == 1 else torch.stack(parts)
+        out["ws1"] = stack(20, (Fs, d), 1.0 / math.sqrt(d))
+        out["ws3"] = stack(21, (Fs, d), 1.0 / math.sqrt(d))
+        out["ws2"] = stack(22, (d, Fs), 1.0 / math.sqrt(Fs))
     return out
 
 
