@@ -44,6 +44,16 @@ ACT = {"relu": 0, "gelu": 1, "swiglu": 2}
 _lib = None
 
 
+def build_sanitized(out: str) -> str:
+    """Compile moe_oracle.c with gcc's AddressSanitizer and UndefinedBehaviorSanitizer
+    into `out` (load it through ORACLE_LIB with gcc's libasan and libubsan preloaded)."""
+    cmd = ["gcc", "-O1", "-g", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-Wall", "-Werror",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer",
+           _SRC, "-o", out, "-lm"]
+    subprocess.check_call(cmd)
+    return out
+
+
 def build(force: bool = False) -> str:
     """Compile moe_oracle.c into liboracle.so with gcc (OpenMP, -O2, no fast-math)."""
     if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):

@@ -11,7 +11,9 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libmoe_hip.so")
+# MOE_HIP_LIB names another build of the same library (the sanitized host
+# build that the CPU tests load); default: the in-tree libmoe_hip.so
+LIB_PATH = os.environ.get("MOE_HIP_LIB") or os.path.join(PKG, "libmoe_hip.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 GATING = {"topk_softmax": 0, "softmax_topk": 1, "switch": 2, "expert_choice": 3}
