@@ -56,16 +56,18 @@ __device__ inline void store8<float>(float *p, const float *v) {
 // with their gates; then, for each 8-element column chunk, it issues the
 // loads of up to kBatch kept rows at once and adds them in slot order, so
 // several loads are in flight per lane.
-constexpr int kMaxSlots = 1024;  // S <= E <= 1024
 constexpr int kBatch = 8;
 template <typename T>
 __global__ __launch_bounds__(256) void combine_kernel(const T *__restrict__ y_perm, const T *__restrict__ y_shared,
                                                       const float *__restrict__ w,
                                                       const int32_t *__restrict__ slot_row, int Tn, int d, int S,
                                                       int expert_choice, int parts, T *__restrict__ y) {
-    __shared__ int32_t krow[4][kMaxSlots];
-    __shared__ float kw[4][kMaxSlots];
+    // per-wave tables of the kept rows and gates, S entries each (dynamic
+    // LDS sized to S, so that few slots leave room for more waves per CU)
+    extern __shared__ int32_t comb_lds[];
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    int32_t *krow = comb_lds + wave * S;
+    float *kw = reinterpret_cast<float *>(comb_lds + 4 * S) + wave * S;
     const int64_t gw = (int64_t)blockIdx.x * 4 + wave;
     const int64_t t = gw / parts;
     if (t >= Tn) return;
@@ -81,8 +83,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const T *__restrict__ y_pe
         const uint64_t m = __ballot(keep);
         if (keep) {
             const int pos = nv + __popcll(m & ((1ull << lane) - 1ull));
-            krow[wave][pos] = row;
-            kw[wave][pos] = expert_choice ? w[row] : w[t * S + s];
+            krow[pos] = row;
+            kw[pos] = expert_choice ? w[row] : w[t * S + s];
         }
         nv += __popcll(m);
     }
@@ -95,11 +97,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const T *__restrict__ y_pe
             float v[kBatch][8];
 #pragma unroll
             for (int b = 0; b < kBatch; ++b)
-                if (j0 + b < nv) load8<T>(y_perm + (int64_t)krow[wave][j0 + b] * d + c0, v[b]);
+                if (j0 + b < nv) load8<T>(y_perm + (int64_t)krow[j0 + b] * d + c0, v[b]);
 #pragma unroll
             for (int b = 0; b < kBatch; ++b)
                 if (j0 + b < nv) {
-                    const float g = kw[wave][j0 + b];
+                    const float g = kw[j0 + b];
 #pragma unroll
                     for (int i = 0; i < 8; ++i) acc[i] = fmaf(g, v[b][i], acc[i]);
                 }
@@ -122,12 +124,13 @@ void launch_combine(const CombineArgs &a, hipStream_t s) {
     const int64_t want = (4LL * device_cus() + a.T - 1) / a.T;
     const int parts = (int)std::max<int64_t>(1, std::min<int64_t>(want, a.d / (kWave * 8)));
     const dim3 grid((unsigned)((a.T * parts + 3) / 4));
+    const size_t lds = (size_t)4 * a.S * (sizeof(int32_t) + sizeof(float));
     if (a.bf16)
-        hipLaunchKernelGGL(combine_kernel<bf16>, grid, dim3(256), 0, s, (const bf16 *)a.y_perm,
+        hipLaunchKernelGGL(combine_kernel<bf16>, grid, dim3(256), lds, s, (const bf16 *)a.y_perm,
                            (const bf16 *)a.y_shared, a.w, a.slot_row, a.T, a.d, a.S, (int)a.expert_choice, parts,
                            (bf16 *)a.y);
     else
-        hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, s, (const float *)a.y_perm,
+        hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), lds, s, (const float *)a.y_perm,
                            (const float *)a.y_shared, a.w, a.slot_row, a.T, a.d, a.S, (int)a.expert_choice, parts,
                            (float *)a.y);
 }

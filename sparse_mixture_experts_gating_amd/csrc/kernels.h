@@ -31,8 +31,13 @@ void launch_gate_logits(const float *logits, int T, int E, int k, int gating, in
 constexpr int kStatTokens = 256;  // tokens per block of the router statistics
 void launch_router_stats(const float *logits, const int32_t *idx, int T, int E, int k, float *part,
                          int32_t *cnt, float *out, hipStream_t s);
+// Expert-choice selection; with slot_row set it also writes what the
+// expert-choice permutation writes (counts, offsets, row_token, slot_row
+// [T][E]) and, with plan.mstart set, the grouped GEMMs' tile plan, so the
+// forward pass needs no permutation launch.  Declared after TilePlanArgs.
+struct EcPermuteArgs;
 void launch_ec_select(const float *logits, int T, int E, int C, int32_t *ec_idx, float *ec_score,
-                      hipStream_t s);
+                      hipStream_t s, const EcPermuteArgs *perm = nullptr);
 
 // ---- permute ----
 struct PermuteArgs {
@@ -61,6 +66,11 @@ struct TilePlanArgs {
     int32_t *cnt;
     int ncnt;
     bool interleave;
+};
+
+struct EcPermuteArgs {
+    int32_t *counts = nullptr, *offsets = nullptr, *row_token = nullptr, *slot_row = nullptr;
+    TilePlanArgs plan{};
 };
 
 // The router of a batch that fits one router block (bf16, token choice,

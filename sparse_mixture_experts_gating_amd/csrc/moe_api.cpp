@@ -748,6 +748,26 @@ moe_status moe_forward(const moe_config *cfg, const void *x, const moe_weights *
         pa.plan = plan;
         TRY(launch(K_ROUTE, s, [&] { launch_route_permute(a, pa, s); }));
         plan_built = true;
+    } else if (D.ec) {
+        // expert choice: the selection kernel also writes the permutation
+        // and the tile plan (every expert has exactly C rows)
+        RouteArgs a{x, w->w_router, w->b_router, (int)D.T, (int)D.d, (int)D.E, (int)D.k, D.gating, D.bf16,
+                    r.logits, r.topk_idx, r.topk_w, nullptr, nullptr};
+        TRY(launch(K_ROUTE, s, [&] { launch_route(a, s); }));
+        EcPermuteArgs pa;
+        pa.counts = r.counts;
+        pa.offsets = r.offsets;
+        pa.row_token = r.row_token;
+        pa.slot_row = r.slot_row;
+        pa.plan = plan;
+        TRY(launch(K_EC_SELECT, s, [&] {
+            launch_ec_select(r.logits, (int)D.T, (int)D.E, D.capacity, r.topk_idx, r.topk_w, s, &pa);
+        }));
+        plan_built = true;
+        if (!fused)
+            TRY(launch(K_GATHER, s, [&] {
+                launch_gather_rows(x, r.row_token, r.offsets, (int)D.E, D.a_max, (int)D.d, (int)D.elem, x_perm, s);
+            }));
     } else {
         TRY(do_route(D, x, w, &r, s));
         TRY(do_permute(D, x, &r, x_perm, base, fw.perm, s, !fused, &plan, &plan_built));

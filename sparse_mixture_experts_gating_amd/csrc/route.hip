@@ -9,6 +9,7 @@
 //             gating formula, TopKGating, ExpertChoiceGating
 #include "common.h"
 #include "kernels.h"
+#include "plan.h"
 #include "perm_small.h"
 
 namespace moe {
@@ -402,7 +403,7 @@ constexpr int kEcColMax = 16384;
 template <bool CACHE>
 __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(const float *__restrict__ logits, int T, int E,
                                                                int C, int32_t *__restrict__ ec_idx,
-                                                               float *__restrict__ ec_score) {
+                                                               float *__restrict__ ec_score, EcPermuteArgs perm) {
     constexpr int NW = kEcThreads / kWave;
     __shared__ float shf[NW];
     __shared__ int shi[NW];
@@ -414,7 +415,21 @@ __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(const float *__re
     const int tid = threadIdx.x, wave = tid / kWave;
     const float *col = logits + e;
     if constexpr (CACHE) {
-        for (int t = tid; t < T; t += kEcThreads) colc[t] = col[(int64_t)t * E];
+        // eight strided loads in flight per thread before their LDS stores
+        // (one at a time, each waited for, the column took most of the kernel)
+        for (int t0 = tid; t0 < T; t0 += 8 * kEcThreads) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int t = t0 + u * kEcThreads;
+                v[u] = t < T ? col[(int64_t)t * E] : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int t = t0 + u * kEcThreads;
+                if (t < T) colc[t] = v[u];
+            }
+        }
         __syncthreads();
     }
     auto val = [&](int t) { return CACHE ? colc[t] : col[(int64_t)t * E]; };
@@ -561,6 +576,39 @@ __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(const float *__re
         const float v = key_value((uint32_t)(kk >> 32));
         ec_idx[(int64_t)e * C + j] = (int32_t)rank_key_index(kk);
         ec_score[(int64_t)e * C + j] = expf(v - m) / z;
+    }
+    if (perm.slot_row == nullptr) return;
+    // The permutation of expert choice: expert e owns rows e*C .. e*C + C - 1
+    // in rank order; column e of slot_row is -1 except at its C tokens.
+    // The -1 fill completes (each thread's stores, then the barrier) before
+    // the rows are written over it.
+    for (int t = tid; t < T; t += kEcThreads) perm.slot_row[(int64_t)t * E + e] = -1;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    for (int j = tid; j < C; j += kEcThreads) {
+        const int t = (int)rank_key_index(cand[j]);
+        perm.row_token[(int64_t)e * C + j] = t;
+        perm.slot_row[(int64_t)t * E + e] = e * C + j;
+    }
+    if (tid == 0) {
+        perm.counts[e] = C;
+        perm.offsets[e] = e * C;
+        if (e == 0) perm.offsets[E] = E * C;
+    }
+    if (e == 0 && perm.plan.mstart != nullptr) {
+        // every expert has C rows: the plan needs no other block's results
+        // counts [E], offsets [E+1] and the plan's 3(E+1) scratch ints in the
+        // candidate buffer (free once every thread has read its rows)
+        static_assert(kEcMaxCapacity * 2 >= 5 * kMaxPlanExperts + 4, "plan scratch fits");
+        int32_t *pc = reinterpret_cast<int32_t *>(cand);
+        __syncthreads();
+        for (int i = tid; i <= E; i += kEcThreads) {
+            if (i < E) pc[i] = C;
+            pc[E + i] = i * C;
+        }
+        __syncthreads();
+        build_tile_plan(pc, pc + E, E, perm.plan.BM, perm.plan.mstart, perm.plan.mtile, perm.plan.max_mt,
+                        perm.plan.cnt, perm.plan.ncnt, perm.plan.interleave, pc + 2 * E + 1);
     }
 }
 
@@ -794,11 +842,14 @@ void launch_gate_logits(const float *logits, int T, int E, int k, int gating, in
 }
 
 void launch_ec_select(const float *logits, int T, int E, int C, int32_t *ec_idx, float *ec_score,
-                      hipStream_t s) {
+                      hipStream_t s, const EcPermuteArgs *perm) {
+    const EcPermuteArgs pa = perm ? *perm : EcPermuteArgs{};
     if (T <= kEcColMax)
-        hipLaunchKernelGGL(ec_select_kernel<true>, dim3(E), dim3(kEcThreads), 0, s, logits, T, E, C, ec_idx, ec_score);
+        hipLaunchKernelGGL(ec_select_kernel<true>, dim3(E), dim3(kEcThreads), 0, s, logits, T, E, C, ec_idx, ec_score,
+                           pa);
     else
-        hipLaunchKernelGGL(ec_select_kernel<false>, dim3(E), dim3(kEcThreads), 0, s, logits, T, E, C, ec_idx, ec_score);
+        hipLaunchKernelGGL(ec_select_kernel<false>, dim3(E), dim3(kEcThreads), 0, s, logits, T, E, C, ec_idx,
+                           ec_score, pa);
 }
 
 }  // namespace moe
