@@ -53,6 +53,8 @@ def kernel_work(spec, counts, name):
     nw = 2 if spec.act == "swiglu" else 1
     if name == "route":
         return 2.0 * T * d * E, eb * (T * d + E * d) + 4.0 * T * E + (0.0 if ec else 8.0 * T * spec.k)
+    if name == "route_gate":  # logits once in and out, selections out (the K-split parts are tiling re-reads)
+        return 0.0, 8.0 * T * E + 8.0 * T * spec.k
     if name == "ec_select":
         return 0.0, 4.0 * T * E + 8.0 * rows
     if name == "permute_count":

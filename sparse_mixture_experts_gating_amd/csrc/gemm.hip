@@ -128,6 +128,11 @@ struct GemmParams {
     // K-sliced B (one group): K = (K / kslice) slices of kslice, slice s a
     // [N][kslice] matrix at B0 + s * N * kslice; 0 = B is [N][K]
     int kslice;
+    // float32 partial products (one group, the router's logits): every tile
+    // is split into fixed_split K parts, and part q writes its [rows][N]
+    // float32 sums to partout + q * rows * N (no activation, no epilogue)
+    float *partout;
+    int fixed_split;
 };
 
 // Work item of one workgroup.  The tiles fill rounds of `slots` workgroups;
@@ -148,6 +153,13 @@ struct WorkItem {
 
 __device__ inline WorkItem work_item(int w, int ntiles, const GemmParams &p) {
     WorkItem it{w, 0, 1, 0, w < ntiles};
+    if (p.fixed_split > 0) {  // every tile in fixed_split K parts, consecutive work items
+        it.tile = w / p.fixed_split;
+        it.part = w % p.fixed_split;
+        it.S = p.fixed_split;
+        it.valid = it.tile < ntiles;
+        return it;
+    }
     if (p.part == nullptr || ntiles <= 0) return it;
     const int rem = ntiles % p.slots;
     if (rem == 0) return it;
@@ -210,8 +222,10 @@ __device__ inline void dispatch_active(int n, F &&f) {
 // MFMA) instead of the A fragment.
 // SL: B is K-sliced (p.kslice > 0): the rows of each K tile are read from
 // its slice (the shared experts' down projections side by side along K).
+// PO: float32 partial products out (p.partout, p.fixed_split): each work
+// item writes its K part's sums and ends there.
 template <int BM, int BN, int WM, int WN, bool GLU, int IL = 0, int MF = 32, bool RMAP = false, int BK = 64,
-          bool JOUT = false, bool SL = false>
+          bool JOUT = false, bool SL = false, bool PO = false>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
     constexpr int NT = 64 * WM * WN;  // threads
     static_assert(BK == 64 || BK == 128, "K tile");
@@ -435,6 +449,26 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
         }
     };
     dispatch_active<0, TM>(nact, kloop);
+
+    if constexpr (PO) {
+        // accumulator r of an MFMA tile holds D[row][lane % MF] with row =
+        // 8*(r/4) + 4*(lane/32) + r%4 (32x32) or 4*(lane/16) + r (16x16)
+        static_assert(!GLU, "partial products of one projection");
+        float *out = p.partout + (int64_t)wi.part * p.rows * p.N;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TB; ++j) {
+                const int col = n0 + wn * WTN + j * MF + lane % MF;
+#pragma unroll
+                for (int r = 0; r < AR; ++r) {
+                    const int64_t row = tc.row0 + wm * WTM + i * MF +
+                                        (MF == 32 ? 8 * (r / 4) + 4 * (lane / 32) + r % 4 : 4 * (lane / 16) + r);
+                    if (row < tc.row_end && col < p.N) out[row * p.N + col] = acc[i][j][r];
+                }
+            }
+        return;
+    }
 
     if (wi.S > 1) {
         // Publish this part's accumulators; the last part to arrive adds the
@@ -728,16 +762,23 @@ static int64_t grid_for(const GemmArgs &a, int BM, int BN) {
 }
 
 template <int BM, int BN, int WM, int WN, bool GLU, int MF = 16, bool RMAP = false, int IL = 0, int BK = 64,
-          bool JOUT = false, bool SL = false>
-static void launch_bf16_t(const GemmArgs &a, hipStream_t s) {
+          bool JOUT = false, bool SL = false, bool PO = false>
+static void launch_bf16_t(const GemmArgs &a, hipStream_t s, float *partout = nullptr, int fixed_split = 0) {
     constexpr int NB = GLU ? 2 * BN : BN;
     static_assert((int64_t)BM * NB <= kSplitUnitFloats, "split-K unit");
-    auto kern = gemm_bf16_kernel<BM, BN, WM, WN, GLU, IL, MF, RMAP, BK, JOUT, SL>;
+    auto kern = gemm_bf16_kernel<BM, BN, WM, WN, GLU, IL, MF, RMAP, BK, JOUT, SL, PO>;
     GemmParams p{(const bf16 *)a.A, (const bf16 *)a.B0, (const bf16 *)a.B1, a.bias, (bf16 *)a.C,
                  a.offsets, a.mstart, a.mtile, a.max_mt, a.G, a.rows, a.N, a.K, a.act, nullptr, nullptr, 0, 1, 0,
-                 a.arow, a.a_rows * a.K * 2, SL ? a.kslice : 0};
+                 a.arow, a.a_rows * a.K * 2, SL ? a.kslice : 0, PO ? partout : nullptr, PO ? fixed_split : 0};
     int64_t grid = grid_for(a, BM, BN);
     if (grid == 0) return;
+    if constexpr (PO) {
+        // every tile in fixed_split parts (consecutive work items), whole grid quanta
+        const int64_t need = ((a.rows + BM - 1) / BM) * ((a.N + BN - 1) / BN) * fixed_split;
+        grid = (need + kGridQuantum - 1) / kGridQuantum * kGridQuantum;
+        hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * WM * WN), 0, s, p);
+        return;
+    }
     // Split K of the last round needs the number of co-resident workgroups
     // and room for that many partial tiles; otherwise it stays off.  Only
     // for K loops of at least 4096 (at least 2048 per part).
@@ -777,6 +818,23 @@ static void launch_f32_t(const GemmArgs &a, hipStream_t s) {
     const int64_t grid = grid_for(a, kF32BM, 32);
     if (grid == 0) return;
     hipLaunchKernelGGL((gemm_f32_kernel<GLU>), dim3((unsigned)grid), dim3(256), 0, s, p);
+}
+
+int router_gemm_split(int T, int E, int d) {
+    // 128-row tiles over all E <= 256 columns; enough K parts for about one
+    // work item per CU, each part at least 512 deep
+    const int tiles = (T + 127) / 128 * ((E + 255) / 256);
+    int cus = device_cus();
+    if (cus <= 0) cus = 256;
+    int S = (cus + tiles - 1) / tiles;
+    S = std::max(1, std::min(S, std::min(kRouterMaxSplit, d / 512)));
+    return S;
+}
+
+void launch_router_gemm(const void *x, const void *wg, int T, int d, int E, float *partout, int S, hipStream_t s) {
+    GemmArgs a{x, wg, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 1, T, E, d, kActNone, true,
+               SplitKWs{nullptr, 0, nullptr, 0}};
+    launch_bf16_t<128, 256, 2, 4, false, 32, true, 1, 64, false, false, true>(a, s, partout, S);
 }
 
 void launch_grouped_gemm(const GemmArgs &a, int shape, hipStream_t s) {

@@ -148,6 +148,14 @@ struct GemmArgs {
     int kslice = 0;
 };
 enum GemmShape { kGemmPrefill = 0, kGemmSmallM = 1, kGemmDecode = 2 };
+// Router logits of many experts as a dense GEMM: x [T][d] times wg [E][d]^T
+// (E <= 256), split into S K parts whose float32 sums go to partout [S][T][E];
+// launch_gate_partials adds them up and gates.
+constexpr int kRouterMaxSplit = 8;
+int router_gemm_split(int T, int E, int d);
+void launch_router_gemm(const void *x, const void *wg, int T, int d, int E, float *partout, int S, hipStream_t s);
+void launch_gate_partials(const float *part, int S, const float *bias, int T, int E, int k, int gating,
+                          float *logits, int32_t *idx, float *w, hipStream_t s);
 int gemm_block_m(int shape, bool bf16);
 void launch_grouped_gemm(const GemmArgs &a, int shape, hipStream_t s);
 

@@ -35,12 +35,13 @@ moe_status fail(moe_status st, const char *fmt, ...) {
 // ---------------------------------------------------------------------------
 enum Kind {
     K_ROUTE, K_GATE_LOGITS, K_EC_SELECT, K_PERM_COUNT, K_PERM_SCAN, K_PERM_SCATTER, K_EC_PERMUTE, K_GATHER,
-    K_TILE_PLAN, K_GEMM1, K_GEMM2, K_GEMM1_SHARED, K_GEMM2_SHARED, K_COMBINE, K_ROUTER_STATS, K_PERM_SMALL, K_COUNT
+    K_TILE_PLAN, K_GEMM1, K_GEMM2, K_GEMM1_SHARED, K_GEMM2_SHARED, K_COMBINE, K_ROUTER_STATS, K_PERM_SMALL,
+    K_ROUTE_GATE, K_COUNT
 };
 const char *kKindNames[K_COUNT] = {"route", "gate_logits", "ec_select", "permute_count", "permute_scan",
                                    "permute_scatter", "ec_permute", "gather_rows", "tile_plan", "gemm1_act",
                                    "gemm2", "gemm1_act_shared", "gemm2_shared", "combine", "router_stats",
-                                   "permute_small"};
+                                   "permute_small", "route_gate"};
 
 struct Pending {
     hipEvent_t a, b;
@@ -259,8 +260,15 @@ FfnWs carve_ffn(const Derived &D, Carve &c) {
     return w;
 }
 
+// Token choice over many experts (bf16, 128..256 experts, at least 1024
+// tokens): the forward pass computes the router logits as a dense GEMM split
+// along K into partial sums (workspace), then one light kernel adds the
+// parts, writes the logits and gates.  The fused tile router would stream all
+// router weights through LDS once per 32 tokens.
+bool router_as_gemm(const Derived &D) { return D.bf16 && !D.ec && D.E >= 128 && D.E <= 256 && D.T >= 1024; }
+
 struct ForwardWs {
-    size_t logits, idx, w, counts, offsets, row_token, slot_row, x_perm, y_perm, y_shared;
+    size_t logits, idx, w, counts, offsets, row_token, slot_row, x_perm, y_perm, y_shared, rpart;
     PermuteWs perm;
     FfnWs ffn;
 };
@@ -278,6 +286,7 @@ ForwardWs carve_forward(const Derived &D, Carve &c) {
     w.y_shared = D.Fs ? c.take((size_t)D.T * D.d * D.elem) : 0;
     w.perm = carve_permute(D, c);
     w.ffn = carve_ffn(D, c);
+    w.rpart = router_as_gemm(D) ? c.take((size_t)kRouterMaxSplit * D.T * D.E * 4) : 0;
     return w;
 }
 
@@ -769,7 +778,19 @@ moe_status moe_forward(const moe_config *cfg, const void *x, const moe_weights *
                 launch_gather_rows(x, r.row_token, r.offsets, (int)D.E, D.a_max, (int)D.d, (int)D.elem, x_perm, s);
             }));
     } else {
-        TRY(do_route(D, x, w, &r, s));
+        if (router_as_gemm(D)) {
+            const int S = router_gemm_split((int)D.T, (int)D.E, (int)D.d);
+            float *part = (float *)(base + fw.rpart);
+            TRY(launch(K_ROUTE, s, [&] {
+                launch_router_gemm(x, w->w_router, (int)D.T, (int)D.d, (int)D.E, part, S, s);
+            }));
+            TRY(launch(K_ROUTE_GATE, s, [&] {
+                launch_gate_partials(part, S, w->b_router, (int)D.T, (int)D.E, (int)D.k, D.gating, r.logits,
+                                     r.topk_idx, r.topk_w, s);
+            }));
+        } else {
+            TRY(do_route(D, x, w, &r, s));
+        }
         TRY(do_permute(D, x, &r, x_perm, base, fw.perm, s, !fused, &plan, &plan_built));
     }
     TRY(do_ffn(D, fused ? nullptr : x_perm, x, &r, w, y_perm, y_shared, base, fw.ffn, s, plan_built));

@@ -233,6 +233,38 @@ __global__ __launch_bounds__(256) void route_f32_kernel(
     if (live && gating != kGateExpertChoice) gate_one_token(rows[wave], E, k, gating, t, idx_out, w_out);
 }
 
+// Logits from the router GEMM's K parts: l[t][e] = sum of the S parts in
+// part order, plus the bias, written out and gated from LDS with the same
+// selection and weights as the fused routers.  One wave per token.
+__global__ __launch_bounds__(256) void gate_partials_kernel(const float *__restrict__ part, int S,
+                                                            const float *__restrict__ bias, int T, int E, int k,
+                                                            int gating, float *__restrict__ logits,
+                                                            int32_t *__restrict__ idx_out, float *__restrict__ w_out) {
+    __shared__ float rows[4][256];
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+    if (t >= T) return;
+    const int64_t slab = (int64_t)T * E;
+    for (int e = lane; e < E; e += kWave) {
+        float v = part[t * E + e];
+        for (int q = 1; q < S; ++q) v += part[q * slab + t * E + e];
+        if (bias) v += bias[e];
+        rows[wave][e] = v;
+        logits[t * E + e] = v;
+    }
+    // gate_one_token reads back the entries each lane wrote; the barrier
+    // keeps the compiler from moving those LDS reads above the writes
+    __builtin_amdgcn_wave_barrier();
+    gate_one_token(rows[wave], E, k, gating, t, idx_out, w_out);
+}
+
+void launch_gate_partials(const float *part, int S, const float *bias, int T, int E, int k, int gating,
+                          float *logits, int32_t *idx, float *w, hipStream_t s) {
+    if (T == 0) return;
+    hipLaunchKernelGGL(gate_partials_kernel, dim3((T + 3) / 4), dim3(256), 0, s, part, S, bias, T, E, k, gating,
+                       logits, idx, w);
+}
+
 // Gating alone on given float32 logits [T][E]: one wave per token.
 __global__ __launch_bounds__(256) void gate_logits_kernel(const float *__restrict__ logits, int T, int E,
                                                            int k, int gating, int32_t *__restrict__ idx_out,

@@ -531,3 +531,42 @@ def test_invalid_arguments_are_rejected_before_launch():
     with pytest.raises(moe.MoEError) as ei:
         moe.moe_forward(cfg, dinp["x"], moe.make_weights(dinp), y, None, ws)
     assert ei.value.status == 3
+
+
+# The forward pass routes many experts (bf16 token choice, 128..256 experts,
+# at least 1024 tokens) with a K-split router GEMM and a separate gating
+# kernel.  Integer inputs keep the logits exact in any summation order, so
+# they, the selections and the permutation must equal the oracle's bit for
+# bit; sampled outputs within tolerance.
+ROUTER_GEMM_SPECS = [
+    workloads.DEEPSEEK_SHARED_BF16.replace(name="router_gemm_d7168_e256_int", T=2048, d=7168, F=64, F_shared=0,
+                                           inputs="integer"),
+    workloads.DEEPSEEK_SHARED_BF16.replace(name="router_gemm_d4096_e128_int", T=1500, d=4096, E=128, k=6, F=64,
+                                           F_shared=128, inputs="integer"),
+]
+
+
+@pytest.mark.parametrize("spec", ROUTER_GEMM_SPECS, ids=lambda s: s.name)
+def test_forward_router_gemm_exact(spec):
+    inp = workloads.make_inputs(spec)
+    dinp = to_dev(inp)
+    moe.moe_timing_reset()
+    moe.moe_timing_enable(True)
+    y, routing = run_forward(spec, dinp)
+    names = moe.moe_kernel_names()
+    launched = {n for i, n in enumerate(names) if moe.moe_timing_read(i)[1]}
+    moe.moe_timing_enable(False)
+    assert "route_gate" in launched
+    lg = oracle.logits(inp["x"], inp["wg"], inp["bg"])
+    assert np.array_equal(_np(routing["logits"]), lg)
+    idx, w = oracle.route_topk(lg, spec.k, spec.gating)
+    assert np.array_equal(_np(routing["topk_idx"]).reshape(spec.T, spec.k), idx)
+    np.testing.assert_allclose(_np(routing["topk_w"]).reshape(spec.T, spec.k), w, rtol=2e-6, atol=1e-30)
+    perm = oracle.permute(idx, spec.E)
+    n = perm["kept"]
+    assert np.array_equal(_np(routing["counts"]), perm["counts"])
+    assert np.array_equal(_np(routing["row_token"])[:n], perm["row_token"])
+    assert np.array_equal(_np(routing["slot_row"]).reshape(spec.T, spec.k), perm["slot_row"])
+    toks = np.array([0, 1, spec.T // 3, spec.T // 2, spec.T - 2, spec.T - 1])
+    ref = oracle.forward_tokens(spec, inp, toks, lg=lg)
+    assert rel_err(_np(y)[toks], ref["y64"]) <= TOL[spec.dtype]
