@@ -12,8 +12,9 @@
 // Tiles: a device-side plan (mstart, m-tile table) lists the m-tiles of every expert; the
 // grid covers the worst case and surplus blocks exit.  Inside an expert with
 // Me m-tiles, tiles run in groups of Me x gN (m fastest, gN ~ 32 / Me weight
-// panels), and every XCD receives runs of 32 consecutive tiles: a run shares
-// the expert's activation tiles and a few weight panels in that XCD's L2.
+// panels; bands of 8 m-tiles when Me > 8), and every XCD receives runs of 32
+// consecutive tiles: a run shares the expert's activation tiles and a few
+// weight panels in that XCD's L2.
 #include <algorithm>
 #include <atomic>
 #include <type_traits>
@@ -41,13 +42,26 @@ struct TileCoord {
     bool valid;
 };
 
-// Position of tile `local` among the mt x ntn tiles of one group.
+// Position of tile `local` among the mt x ntn tiles of one group.  A group
+// of more than kBandM m-tiles is cut into bands of kBandM m-tiles (the last
+// one shorter), each band's tiles in runs of kBandM x 32/kBandM; so a run of
+// 32 never holds 32 m-tiles of one weight panel, which would re-read the
+// group's activation rows once per panel (DeepSeek-style shared experts,
+// 32 m-tiles x 16 panels: gate/up 392 -> 382 us, down 300 -> 291 us).
+constexpr int kBandM = 8;
 __device__ inline void group_tile(int local, int mt, int ntn, int *m, int *n) {
+    int mb0 = 0;  // first m-tile of the band
+    if (mt > kBandM) {
+        const int b = local / (kBandM * ntn);
+        mb0 = b * kBandM;
+        local -= b * kBandM * ntn;
+        mt = min(kBandM, mt - mb0);
+    }
     int gn = kXcdRun / mt;
     if (gn < 1) gn = 1;
     const int per = mt * gn;
     const int grp = local / per, within = local % per;
-    *m = within % mt;
+    *m = mb0 + within % mt;
     *n = grp * gn + within / mt;
 }
 
@@ -297,11 +311,16 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
     const __amdgpu_buffer_rsrc_t b0rsrc =
         buffer_rsrc(b0base, SL ? ((K / bstride) * p.N - n0) * bstride * 2 : (int64_t)(p.N - n0) * K * 2);
     const __amdgpu_buffer_rsrc_t b1rsrc = GLU ? buffer_rsrc(b1base, (int64_t)(p.N - n0) * K * 2) : b0rsrc;
-    // byte offset of K tile kt (of this work item) inside B: its slice, then its column
+    // byte offset of K tile kt (of this work item) inside B: its slice, then
+    // its column.  The slice width is a multiple of BK, and all of B spans
+    // less than 2^31 bytes, so 32-bit tile arithmetic suffices (a 64-bit
+    // division per K tile had cost the 256-row kernel 103 spilled VGPRs).
+    const int tps = SL ? p.kslice / BK : 1;              // K tiles per slice
+    const int slice_bytes = SL ? p.N * p.kslice * 2 : 0;  // bytes per slice
     auto bk_off = [&](int kt) {
         if constexpr (SL) {
-            const int64_t kk = (int64_t)(kbeg + kt) * BK;
-            return (int)((kk / bstride) * p.N * bstride * 2 + (kk % bstride) * 2);
+            const int t = kbeg + kt;
+            return (t / tps) * slice_bytes + (t % tps) * (BK * 2);
         } else {
             return kt * BK * 2;
         }
@@ -580,6 +599,276 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
     }
 }
 
+// 16 bytes per lane from a buffer straight into LDS: lane l writes bytes
+// 16 l .. 16 l + 15 after the wave-uniform LDS address `dst` (one wave
+// instruction fills 1 KiB); offsets at or past the buffer's limit write zeros.
+__device__ __forceinline__ void buffer_load16_lds(__amdgpu_buffer_rsrc_t r, bf16 *dst, uint32_t voff, int soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)dst, 16, voff, soff, 0, 0);
+}
+
+// Gate/up GEMM of the 256-row tiles with its operands loaded from global
+// memory straight into LDS (buffer_load_dwordx4 ... lds), so that no
+// registers stage them: the register-staged kernel above spends 64 VGPRs a
+// thread on its two load sets.  8 waves (2 per SIMD) in 2 (rows) x 4
+// (columns); each wave 128 rows x (32 gate + 32 up) columns on
+// v_mfma_f32_16x16x32_bf16, with the fragments double-buffered.  Waves w and
+// w + 4, which share a SIMD, take different row halves, and in a tile of
+// fewer than BM rows each wave runs only its row blocks that hold rows (as
+// above).  Each load instruction fills RPI whole LDS rows, and every lane
+// fetches the 16-byte chunk that its swizzled slot holds.
+//
+// Two LDS buffers, one barrier per K tile (two k-substeps of 32):
+//   1. the MFMAs of substep 0 (fragments in slot 0), with the fragment
+//      reads of substep 1 into slot 1 between them;
+//   2. wait for this wave's loads of tile kt+1 and its reads of tile kt;
+//      barrier, so every wave's loads have landed and every wave has read
+//      tile kt;
+//   3. the MFMAs of substep 1, with the loads of tile kt+2 into tile kt's
+//      buffer and the substep-0 reads of tile kt+1 into slot 0 between them.
+// The program order of each MFMA batch is pinned in groups (sched_barrier):
+// group g issues load g, then fragment reads 3g .. 3g+2, then its share of
+// the MFMAs (B fragment in the outer loop).  K runs in pairs of K tiles, so
+// K % 128 == 0, and split parts cut on pairs.
+//
+// Alternating launches against the register-staged kernel: Mixtral-shape
+// gate/up 1703 -> 1606 us, DeepSeek-style shared experts 392 -> 341 us,
+// DeepSeek-style routed gate/up unchanged (4391 -> 4435 us).  Fragment reads
+// 2 or 4 per group instead of 3: 1% and 4% slower.  The same schedule on the
+// down projection gained nothing (880 -> 888 us), so that one stays
+// register-staged.
+template <int BM, int BN>
+__global__ __launch_bounds__(512) void gemm_swiglu_lds_kernel(GemmParams p) {
+    constexpr int WM = 2, WN = 4, NT = 64 * WM * WN, NW = WM * WN;
+    constexpr int BK = 64, NB = 2 * BN;  // B rows of a tile: BN gate rows, then BN up rows
+    constexpr int WTM = BM / WM, WTB = NB / WN;
+    constexpr int MF = 16, KSUB = 32;
+    constexpr int TM = WTM / MF, TB = WTB / MF, TN = TB / 2;
+    constexpr int KCH = BK / 8, RPI = 64 / KCH;          // 16-byte chunks a row; rows a load instruction fills
+    constexpr int AI = BM / RPI / NW, BI = NB / RPI / NW;  // load instructions per wave and K tile
+    constexpr int RPG = 3;                                 // fragment reads per group
+    static_assert(AI >= 1 && BI >= 1 && BK / KSUB == 2, "tile");
+    static_assert(BN % (BI * RPI) == 0, "a wave's B load rows lie in one of gate / up");
+    // two LDS objects, so that the compiler sees that the fragment reads of
+    // one buffer do not alias the direct loads into the other
+    __shared__ __attribute__((aligned(16))) bf16 lds0[(BM + NB) * BK];
+    __shared__ __attribute__((aligned(16))) bf16 lds1[(BM + NB) * BK];
+    __shared__ int last_part;
+
+    const int ntn = (p.N + BN - 1) / BN;
+    const WorkItem wi = work_item(xcd_remap(blockIdx.x), total_tiles(BM, ntn, p.offsets, p.mstart, p.G, p.rows), p);
+    if (!wi.valid) return;
+    const TileCoord tc = find_tile<BM, MF>(wi.tile, p.offsets, p.mstart, p.mtile, p.max_mt, p.G, p.rows, ntn);
+    if (!tc.valid) return;
+    const int n0 = tc.nt * BN;
+    const int64_t K = p.K;
+    const int KP_all = p.K / (2 * BK);
+    const int kbeg = 2 * (int)((int64_t)KP_all * wi.part / wi.S);
+    const int KT = 2 * (int)((int64_t)KP_all * (wi.part + 1) / wi.S) - kbeg;
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
+    const int wm = wave / WN, wn = wave % WN;
+    const int64_t wrows = tc.row_end - (tc.row0 + (int64_t)wm * WTM);
+    const int nact = wrows <= 0 ? 0 : (wrows >= WTM ? TM : (int)((wrows + MF - 1) / MF));
+
+    // buffer resources and byte offsets as in the register-staged kernel
+    const int64_t k0 = (int64_t)kbeg * BK;
+    const char *abase = p.arow ? (const char *)(p.A + k0) : (const char *)(p.A + tc.row0 * K + k0);
+    const __amdgpu_buffer_rsrc_t arsrc =
+        buffer_rsrc(abase, p.arow ? p.a_bytes - k0 * 2 : (tc.row_end - tc.row0) * K * 2);
+    const bool bup = wave * BI * RPI >= BN;  // this wave loads up rows (else gate rows)
+    const bf16 *bmat = bup ? p.B1 : p.B0;
+    const __amdgpu_buffer_rsrc_t brsrc =
+        buffer_rsrc(bmat + ((int64_t)tc.g * p.N + n0) * K + k0, (int64_t)(p.N - n0) * K * 2);
+    // lane L of a load instruction fills LDS row RPI*q + L/KCH, slot L%KCH,
+    // with the global chunk that slot holds: chunk = slot ^ swz(row)
+    const int lrow = lane / KCH, lslot = lane % KCH;
+    uint32_t aoff[AI], boff[BI];
+#pragma unroll
+    for (int i = 0; i < AI; ++i) {
+        const int r = (wave * AI + i) * RPI + lrow;
+        const int c = lslot ^ swz_k<BK>(r);
+        if (p.arow == nullptr) aoff[i] = (uint32_t)(((int64_t)r * K + c * 8) * 2);
+        else aoff[i] = (tc.row0 + r < tc.row_end ? (uint32_t)(p.arow[tc.row0 + r] * K * 2) : 0x80000000u) + c * 16;
+    }
+#pragma unroll
+    for (int i = 0; i < BI; ++i) {
+        const int r = (wave * BI + i) * RPI + lrow;  // LDS B row
+        const int c = lslot ^ swz_k<BK>(r);
+        boff[i] = (uint32_t)(((int64_t)(r % BN) * K + c * 8) * 2);
+    }
+    auto load_a = [&](bf16 *L, int i, int ko) __attribute__((always_inline)) {
+        buffer_load16_lds(arsrc, L + (wave * AI + i) * RPI * BK, aoff[i], ko);
+    };
+    auto load_b = [&](bf16 *L, int i, int ko) __attribute__((always_inline)) {
+        buffer_load16_lds(brsrc, L + BM * BK + (wave * BI + i) * RPI * BK, boff[i], ko);
+    };
+    auto issue = [&](int kt, bf16 *L) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < AI; ++i) load_a(L, i, kt * BK * 2);
+#pragma unroll
+        for (int i = 0; i < BI; ++i) load_b(L, i, kt * BK * 2);
+    };
+    // fragment lanes: row lane % 16 of each 16-row block, 16-byte k chunk
+    // lane / 16 of a 32-k substep; B rows: gate wn*32 .., up BN + wn*32 ..
+    const int sw_a = swz_k<BK>(wm * WTM + lane % MF);
+    const int sw_b = swz_k<BK>(wn * TN * MF + lane % MF);
+    const int fa0 = (wm * WTM + lane % MF) * BK;
+    const int fb0 = (BM + wn * TN * MF + lane % MF) * BK;
+    auto bofs = [](int j) __attribute__((always_inline)) { return ((j >= TN ? BN : 0) + (j % TN) * MF) * BK; };
+
+    f32x4 acc[TM][TB];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TB; ++j) acc[i][j] = f32x4{};
+    bf16x8 fa[2][TM], fb[2][TB];
+    // one MFMA batch (substep of slot ms), with the fragment reads of slot
+    // rs (buffer R, substep rks) and, if LOADS, the loads of tile ldkt into
+    // LD between its MFMAs
+    auto batch = [&](const bf16 *R, int rks, int rs, int ms, bf16 *LD, int ldkt, auto na, auto loads)
+                     __attribute__((always_inline)) {
+        constexpr int NA = decltype(na)::value;
+        constexpr int NR = NA + TB, NM = NA * TB, NL = decltype(loads)::value ? AI + BI : 0;
+        constexpr int NG = NR > NL ? NR : NL;
+        constexpr int PER = (NM + NG - 1) / NG;
+        const int ch = rks * (KSUB / 8) + lane / MF;
+        const bf16 *La = R + fa0 + ((ch ^ sw_a) * 8);
+        const bf16 *Lb = R + fb0 + ((ch ^ sw_b) * 8);
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            if (g < NL) {
+                if (g < AI) load_a(LD, g, ldkt * BK * 2);
+                else load_b(LD, g - AI, ldkt * BK * 2);
+            }
+#pragma unroll
+            for (int r = g * RPG; r < (g + 1) * RPG && r < NR; ++r) {
+                if (r < NA) fa[rs][r] = __builtin_bit_cast(bf16x8, load16(La + r * MF * BK));
+                else fb[rs][r - NA] = __builtin_bit_cast(bf16x8, load16(Lb + bofs(r - NA)));
+            }
+#pragma unroll
+            for (int q = g * PER; q < (g + 1) * PER && q < NM; ++q)
+                acc[q % NA][q / NA] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[ms][q % NA], fb[ms][q / NA],
+                                                                               acc[q % NA][q / NA], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    // K tile kt in buffer L, tile kt+1 landing in Lo; substep 0's fragments
+    // of tile kt are in slot 0
+    auto step = [&](bf16 *L, bf16 *Lo, int kt, auto na) __attribute__((always_inline)) {
+        constexpr bool MMA = decltype(na)::value > 0;
+        if constexpr (MMA) {
+            // slot 0's reads (issued a whole batch ago) are complete; saying
+            // so here keeps the compiler from waiting on the reads it issues
+            // next (the LDS counter saturates at 15 outstanding)
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+            __builtin_amdgcn_sched_barrier(0);
+            batch(L, 1, 1, 0, L, 0, na, std::false_type{});
+        }
+        __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+        __syncthreads();
+        // past the last tile the loads re-read tile KT-1 into a buffer that
+        // nobody reads afterwards (no branches around the loads)
+        if constexpr (MMA) batch(Lo, 0, 0, 1, L, min(kt + 2, KT - 1), na, std::true_type{});
+        else issue(min(kt + 2, KT - 1), L);
+    };
+    // the K loop with the MFMA work of the first NA row blocks of this wave
+    // (loads and barriers are the same for every NA)
+    auto kloop = [&](auto na) __attribute__((always_inline)) {
+        constexpr int NA = decltype(na)::value;
+        issue(0, lds0);
+        issue(min(1, KT - 1), lds1);
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (AI + BI));  // vmcnt(AI+BI): tile 0 landed
+        __syncthreads();
+        if constexpr (NA > 0) {
+            const bf16 *La = lds0 + fa0 + (((lane / MF) ^ sw_a) * 8);
+            const bf16 *Lb = lds0 + fb0 + (((lane / MF) ^ sw_b) * 8);
+#pragma unroll
+            for (int i = 0; i < NA; ++i) fa[0][i] = __builtin_bit_cast(bf16x8, load16(La + i * MF * BK));
+#pragma unroll
+            for (int j = 0; j < TB; ++j) fb[0][j] = __builtin_bit_cast(bf16x8, load16(Lb + bofs(j)));
+        }
+        for (int kt = 0; kt < KT; kt += 2) {
+            step(lds0, lds1, kt, na);
+            step(lds1, lds0, kt + 1, na);
+        }
+        __builtin_amdgcn_s_waitcnt(0x0070);  // the last loads have landed before the LDS is reused
+    };
+    dispatch_active<0, TM>(nact, kloop);
+
+    if (wi.S > 1) {
+        // split K: as in the register-staged kernel (device-scope partials,
+        // the last part to arrive adds them in part order)
+        constexpr int PER_UNIT = BM * NB;
+        constexpr int kDeviceScope = 16;
+        const float *parts = p.part + (int64_t)wi.unit * wi.S * PER_UNIT;
+        const __amdgpu_buffer_rsrc_t prs = buffer_rsrc(parts, (int64_t)wi.S * PER_UNIT * 4);
+        const int mine = wi.part * PER_UNIT * 4;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TB; ++j) {
+                const int o = ((i * TB + j) * NT + tid) * 16;
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), prs, o, mine,
+                                                       kDeviceScope);
+            }
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        __syncthreads();
+        if (tid == 0) last_part = atomicAdd(p.cnt + wi.unit, 1) == wi.S - 1;
+        __syncthreads();
+        if (!last_part) return;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TB; ++j) {
+                const int o = ((i * TB + j) * NT + tid) * 16;
+                f32x4 v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(prs, o, 0, kDeviceScope));
+                for (int sp = 1; sp < wi.S; ++sp)
+                    v += __builtin_bit_cast(
+                        f32x4, __builtin_amdgcn_raw_buffer_load_b128(prs, o, sp * PER_UNIT * 4, kDeviceScope));
+                acc[i][j] = v;
+            }
+        if (tid == 0) p.cnt[wi.unit] = 0;
+    }
+
+    // Epilogue as in the register-staged kernel: silu(gate) * up, bf16
+    // pairs traded between lanes l and l^1, the tile staged in LDS (rows
+    // 0 .. BM/2-1 in lds0, the rest in lds1) for 16-byte row stores.
+    static_assert(BM / 2 * BN * 2 <= (int)sizeof(lds0), "half the output tile fits in a staging buffer");
+    constexpr int CPR = BN / 8;
+    auto Ct = [&](int r) __attribute__((always_inline)) { return r < BM / 2 ? lds0 + r * BN : lds1 + (r - BM / 2) * BN; };
+    const bool odd = lane & 1;
+    auto swap1 = [](float x) {
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+    };
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int cl = wn * TN * MF + j * MF + lane % MF;
+            float v[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = silu_fast(acc[i][j][r]) * acc[i][TN + j][r];
+            const float xs = swap1(odd ? v[0] : v[2]), ys = swap1(odd ? v[1] : v[3]);
+            const int rb = wm * WTM + i * MF + 4 * (lane / 16);
+            const int ra0 = rb + (odd ? 2 : 0), ra1 = ra0 + 1;
+            const int ce = cl & ~1;
+            const bf16x2 p0 = {(bf16)(odd ? xs : v[0]), (bf16)(odd ? v[2] : xs)};
+            const bf16x2 p1 = {(bf16)(odd ? ys : v[1]), (bf16)(odd ? v[3] : ys)};
+            *(bf16x2 *)(Ct(ra0) + (((ce / 8) ^ ((ra0 / 2) & 7)) * 8) + ce % 8) = p0;
+            *(bf16x2 *)(Ct(ra1) + (((ce / 8) ^ ((ra1 / 2) & 7)) * 8) + ce % 8) = p1;
+        }
+    __syncthreads();
+    for (int q = tid; q < BM * CPR; q += NT) {
+        const int rl = q / CPR, c = q % CPR;
+        const int64_t row = tc.row0 + rl;
+        const int col = n0 + c * 8;
+        if (row < tc.row_end && col < p.N)
+            store16(p.C + row * p.N + col, load16(Ct(rl) + ((c ^ ((rl / 2) & 7)) * 8)));
+    }
+}
+
 struct GemmParamsF32 {
     const float *A;
     const float *B0;
@@ -761,6 +1050,36 @@ static int64_t grid_for(const GemmArgs &a, int BM, int BN) {
     return g;
 }
 
+// Split K of the last round needs the number of co-resident workgroups of
+// `kern` (nthreads a workgroup; cached in per_cu_cache) and room for that
+// many BM x NB partial tiles; otherwise it stays off.  Only for K loops of
+// at least 4096 (at least 2048 per part).  Sets p's split fields and returns
+// the workgroups to add to the grid.
+static int64_t split_k_setup(const GemmArgs &a, void (*kern)(GemmParams), int nthreads, int BM, int NB, int BK,
+                             std::atomic<int> &per_cu_cache, GemmParams &p) {
+    const int KT = a.K / BK;
+    const int min_part = 2048 / BK;  // K tiles per part at least (1024 or 512 measured slower on decode tiles)
+    if (a.split.part == nullptr || KT < 2 * min_part) return 0;
+    int per_cu = per_cu_cache.load(std::memory_order_relaxed);
+    if (per_cu < 0) {
+        int n = 0;
+        per_cu = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, nthreads, 0) == hipSuccess ? n : 0;
+        per_cu_cache.store(per_cu, std::memory_order_relaxed);
+    }
+    const int64_t slots = (int64_t)device_cus() * per_cu;
+    if (slots <= 0 || slots > a.split.ncnt || slots * BM * NB > a.split.part_floats) return 0;
+    p.part = a.split.part;
+    p.cnt = a.split.cnt;
+    p.slots = (int)slots;
+    p.max_split = std::min(8, KT / min_part);
+    p.max_slabs = (int)std::min<int64_t>(a.split.part_floats / ((int64_t)BM * NB), 1 << 30);
+    // the split parts add rem * (S - 1) work items beyond the tiles, fewer
+    // than slots * (max_split - 1) and than max_slabs (rem * S slabs);
+    // surplus workgroups exit at once
+    const int64_t extra = std::min<int64_t>(slots * std::max(1, p.max_split - 1), p.max_slabs);
+    return (extra + kGridQuantum - 1) / kGridQuantum * kGridQuantum;
+}
+
 template <int BM, int BN, int WM, int WN, bool GLU, int MF = 16, bool RMAP = false, int IL = 0, int BK = 64,
           bool JOUT = false, bool SL = false, bool PO = false>
 static void launch_bf16_t(const GemmArgs &a, hipStream_t s, float *partout = nullptr, int fixed_split = 0) {
@@ -779,36 +1098,26 @@ static void launch_bf16_t(const GemmArgs &a, hipStream_t s, float *partout = nul
         hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * WM * WN), 0, s, p);
         return;
     }
-    // Split K of the last round needs the number of co-resident workgroups
-    // and room for that many partial tiles; otherwise it stays off.  Only
-    // for K loops of at least 4096 (at least 2048 per part).
-    const int KT = a.K / BK;
-    constexpr int min_part = 2048 / BK;  // K tiles per part at least (1024 or 512 measured slower on decode tiles)
-    if (a.split.part != nullptr && KT >= 2 * min_part) {
-        // workgroups of this kernel per CU, queried once (atomic: callers may
-        // launch from several host threads)
-        static std::atomic<int> per_cu_cache{-1};
-        int per_cu = per_cu_cache.load(std::memory_order_relaxed);
-        if (per_cu < 0) {
-            int n = 0;
-            per_cu = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, 64 * WM * WN, 0) == hipSuccess ? n : 0;
-            per_cu_cache.store(per_cu, std::memory_order_relaxed);
-        }
-        const int64_t slots = (int64_t)device_cus() * per_cu;
-        if (slots > 0 && slots <= a.split.ncnt && slots * BM * NB <= a.split.part_floats) {
-            p.part = a.split.part;
-            p.cnt = a.split.cnt;
-            p.slots = (int)slots;
-            p.max_split = std::min(8, KT / min_part);
-            p.max_slabs = (int)std::min<int64_t>(a.split.part_floats / ((int64_t)BM * NB), 1 << 30);
-            // the split parts add rem * (S - 1) work items beyond the tiles,
-            // fewer than slots * (max_split - 1) and than max_slabs (rem * S
-            // slabs); surplus workgroups exit at once
-            const int64_t extra = std::min<int64_t>(slots * std::max(1, p.max_split - 1), p.max_slabs);
-            grid += (extra + kGridQuantum - 1) / kGridQuantum * kGridQuantum;
-        }
-    }
+    // workgroups of this kernel per CU, queried once (atomic: callers may
+    // launch from several host threads)
+    static std::atomic<int> per_cu_cache{-1};
+    grid += split_k_setup(a, kern, 64 * WM * WN, BM, NB, BK, per_cu_cache, p);
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * WM * WN), 0, s, p);
+}
+
+// SwiGLU gate/up on 256-row tiles with direct-to-LDS loads (K % 128 == 0)
+static void launch_swiglu_lds(const GemmArgs &a, hipStream_t s) {
+    constexpr int BM = 256, BN = 128;
+    static_assert((int64_t)BM * 2 * BN <= kSplitUnitFloats, "split-K unit");
+    auto kern = gemm_swiglu_lds_kernel<BM, BN>;
+    GemmParams p{(const bf16 *)a.A, (const bf16 *)a.B0, (const bf16 *)a.B1, nullptr, (bf16 *)a.C,
+                 a.offsets, a.mstart, a.mtile, a.max_mt, a.G, a.rows, a.N, a.K, a.act, nullptr, nullptr, 0, 1, 0,
+                 a.arow, a.a_rows * a.K * 2, 0, nullptr, 0};
+    int64_t grid = grid_for(a, BM, BN);
+    if (grid == 0) return;
+    static std::atomic<int> per_cu_cache{-1};
+    grid += split_k_setup(a, kern, 512, BM, 2 * BN, 64, per_cu_cache, p);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(512), 0, s, p);
 }
 
 template <bool GLU>
@@ -891,7 +1200,8 @@ void launch_grouped_gemm(const GemmArgs &a, int shape, hipStream_t s) {
         if (glu) launch_bf16_t<128, 128, 2, 4, true, 32, true, 1>(a, s);
         else launch_bf16_t<128, 256, 2, 4, false, 32, true, 1>(a, s);
     } else {
-        if (glu) launch_bf16_t<256, 128, 2, 4, true, 16, true, 1, 64, true>(a, s);
+        if (glu && a.K % 128 == 0) launch_swiglu_lds(a, s);
+        else if (glu) launch_bf16_t<256, 128, 2, 4, true, 16, true, 1, 64, true>(a, s);
         else launch_bf16_t<256, 256, 2, 4, false, 16, true, 1>(a, s);
     }
 }

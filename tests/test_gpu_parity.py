@@ -256,7 +256,15 @@ ABI_SPECS = [
     workloads.DEEPSEEK_SHARED_BF16.replace(name="two_shared_experts_split_k", T=520, d=512, E=64, F=64,
                                            F_shared=2048, num_shared=2),
 ]
-FFN_SPECS = FFN_SPECS + LONG_K_SPECS + SPLITK_SPECS + ABI_SPECS
+# Tile paths of the 256-row SwiGLU gate/up GEMM: K % 128 == 0 takes the
+# direct-to-LDS kernel, other K the register-staged one; an expert (and a
+# shared expert) of more than 8 m-tiles runs its tiles in bands of 8 m-tiles.
+TILE_SPECS = [
+    workloads.MIXTRAL_PREFILL_BF16.replace(name="prefill_tiles_k_not_multiple_of_128", T=1000, d=320, F=384),
+    workloads.DEEPSEEK_SHARED_BF16.replace(name="banded_tiles_shared_expert", T=3000, d=256, E=16, k=2, F=64,
+                                           F_shared=512),
+]
+FFN_SPECS = FFN_SPECS + LONG_K_SPECS + SPLITK_SPECS + ABI_SPECS + TILE_SPECS
 
 
 @pytest.mark.parametrize("spec", FFN_SPECS, ids=lambda s: s.name)
@@ -433,7 +441,7 @@ def _check_layer(spec, inp, y, routing, ref):
     return (~ok).sum()
 
 
-@pytest.mark.parametrize("spec", workloads.SMALL + ABI_SPECS, ids=lambda s: s.name)
+@pytest.mark.parametrize("spec", workloads.SMALL + ABI_SPECS + TILE_SPECS, ids=lambda s: s.name)
 def test_forward_matches_oracle(spec):
     inp = workloads.make_inputs(spec)
     y, routing = run_forward(spec, to_dev(inp))
