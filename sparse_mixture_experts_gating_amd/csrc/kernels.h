@@ -24,8 +24,16 @@ struct RouteArgs {
     float *w;
     const void *wn;       // noisy router: noise projection [E][d], else null
     const float *noise;   // noisy router: [T][E] standard-normal draw, else null
+    // expert choice in the forward pass (bf16 routers): also write the
+    // logits transposed, [E][T], so that each expert's column is contiguous
+    // for the selection, and fill the row map [T][E] with -1 (the selection
+    // then writes only its chosen entries); null: neither
+    float *logits_t = nullptr;
+    int32_t *fill_rows = nullptr;
 };
-void launch_route(const RouteArgs &a, hipStream_t s);
+// Returns whether it wrote logits_t and fill_rows (bf16 routers whose tile
+// has room for the transposed logits; false when logits_t is null).
+bool launch_route(const RouteArgs &a, hipStream_t s);
 void launch_gate_logits(const float *logits, int T, int E, int k, int gating, int32_t *idx, float *w,
                         hipStream_t s);
 constexpr int kStatTokens = 256;  // tokens per block of the router statistics
@@ -36,8 +44,9 @@ void launch_router_stats(const float *logits, const int32_t *idx, int T, int E, 
 // [T][E]) and, with plan.mstart set, the grouped GEMMs' tile plan, so the
 // forward pass needs no permutation launch.  Declared after TilePlanArgs.
 struct EcPermuteArgs;
+// logits_t: the same logits transposed ([E][T], from the router), or null.
 void launch_ec_select(const float *logits, int T, int E, int C, int32_t *ec_idx, float *ec_score,
-                      hipStream_t s, const EcPermuteArgs *perm = nullptr);
+                      hipStream_t s, const EcPermuteArgs *perm = nullptr, const float *logits_t = nullptr);
 
 // ---- permute ----
 struct PermuteArgs {
@@ -71,6 +80,7 @@ struct TilePlanArgs {
 struct EcPermuteArgs {
     int32_t *counts = nullptr, *offsets = nullptr, *row_token = nullptr, *slot_row = nullptr;
     TilePlanArgs plan{};
+    bool prefilled = false;  // slot_row already holds -1 everywhere (written by the router)
 };
 
 // The router of a batch that fits one router block (bf16, token choice,

@@ -268,7 +268,7 @@ FfnWs carve_ffn(const Derived &D, Carve &c) {
 bool router_as_gemm(const Derived &D) { return D.bf16 && !D.ec && D.E >= 128 && D.E <= 256 && D.T >= 1024; }
 
 struct ForwardWs {
-    size_t logits, idx, w, counts, offsets, row_token, slot_row, x_perm, y_perm, y_shared, rpart;
+    size_t logits, idx, w, counts, offsets, row_token, slot_row, x_perm, y_perm, y_shared, rpart, logits_t;
     PermuteWs perm;
     FfnWs ffn;
 };
@@ -287,6 +287,8 @@ ForwardWs carve_forward(const Derived &D, Carve &c) {
     w.perm = carve_permute(D, c);
     w.ffn = carve_ffn(D, c);
     w.rpart = router_as_gemm(D) ? c.take((size_t)kRouterMaxSplit * D.T * D.E * 4) : 0;
+    // expert choice (bf16 routers): the logits transposed, [E][T]
+    w.logits_t = D.ec && D.bf16 ? c.take((size_t)D.T * D.E * 4) : 0;
     return w;
 }
 
@@ -758,19 +760,27 @@ moe_status moe_forward(const moe_config *cfg, const void *x, const moe_weights *
         TRY(launch(K_ROUTE, s, [&] { launch_route_permute(a, pa, s); }));
         plan_built = true;
     } else if (D.ec) {
-        // expert choice: the selection kernel also writes the permutation
-        // and the tile plan (every expert has exactly C rows)
+        // expert choice: the router also writes the logits transposed (each
+        // expert's column contiguous) and fills the row map with -1; the
+        // selection kernel then writes the permutation's chosen entries and
+        // the tile plan (every expert has exactly C rows)
         RouteArgs a{x, w->w_router, w->b_router, (int)D.T, (int)D.d, (int)D.E, (int)D.k, D.gating, D.bf16,
                     r.logits, r.topk_idx, r.topk_w, nullptr, nullptr};
-        TRY(launch(K_ROUTE, s, [&] { launch_route(a, s); }));
+        float *lt = D.bf16 ? (float *)(base + fw.logits_t) : nullptr;
+        a.logits_t = lt;
+        a.fill_rows = lt ? r.slot_row : nullptr;
+        bool transposed = false;
+        TRY(launch(K_ROUTE, s, [&] { transposed = launch_route(a, s); }));
         EcPermuteArgs pa;
         pa.counts = r.counts;
         pa.offsets = r.offsets;
         pa.row_token = r.row_token;
         pa.slot_row = r.slot_row;
         pa.plan = plan;
+        pa.prefilled = transposed;
         TRY(launch(K_EC_SELECT, s, [&] {
-            launch_ec_select(r.logits, (int)D.T, (int)D.E, D.capacity, r.topk_idx, r.topk_w, s, &pa);
+            launch_ec_select(r.logits, (int)D.T, (int)D.E, D.capacity, r.topk_idx, r.topk_w, s, &pa,
+                             transposed ? lt : nullptr);
         }));
         plan_built = true;
         if (!fused)

@@ -101,7 +101,8 @@ __global__ __launch_bounds__(64 * WK) void route_bf16_kernel(
     const bf16 *__restrict__ x, const bf16 *__restrict__ wg, const float *__restrict__ bias,
     int T, int d, int E, int k, int gating, float *__restrict__ logits,
     int32_t *__restrict__ idx_out, float *__restrict__ w_out, const bf16 *__restrict__ wn,
-    const float *__restrict__ noise, RoutePermuteArgs perm) {
+    const float *__restrict__ noise, RoutePermuteArgs perm, float *__restrict__ logits_t,
+    int32_t *__restrict__ fill_rows) {
     constexpr int TOK = 16;
     constexpr int EP = 16 * NT;
     constexpr int LD = EP + 4;
@@ -189,7 +190,19 @@ __global__ __launch_bounds__(64 * WK) void route_bf16_kernel(
         part[tt * LD + e] = s;
     }
     __syncthreads();
-    if (gating == kGateExpertChoice) return;
+    if (gating == kGateExpertChoice) {
+        if (logits_t) {
+            // transposed logits (16 consecutive tokens of each expert) and
+            // the -1 fill of these tokens' rows of the row map
+            for (int i = threadIdx.x; i < TOK * E; i += 64 * WK) {
+                const int e = i / TOK, tt = i % TOK;
+                if (tok0 + tt < T) logits_t[(int64_t)e * T + tok0 + tt] = part[tt * LD + e];
+            }
+            for (int i = threadIdx.x; i < TOK * E; i += 64 * WK)
+                if (tok0 + i / E < T) fill_rows[tok0 * E + i] = -1;
+        }
+        return;
+    }
     for (int tt = wk; tt < TOK; tt += WK) {
         const int64_t t = tok0 + tt;
         if (t < T) gate_one_token(part + tt * LD, E, k, gating, t, idx_out, w_out);
@@ -377,53 +390,46 @@ void launch_router_stats(const float *logits, const int32_t *idx, int T, int E, 
 // Expert choice ([yj-zh] ExpertChoiceRouter; [yj-ja] ExpertChoiceGating):
 // block e scores every token with softmax over the token axis of column e
 // and keeps the C best tokens by (logit desc, token asc).
-//   1. column max m and sum z of exp(l - m) (fixed-order block reductions);
-//   2. radix select (4 x 8-bit digits of the order key) of the C-th key;
-//   3. ordered compaction: keys above the threshold, then the lowest-index
+//   1. radix select (4 x 8-bit digits of the order key) of the C-th key
+//      over the tokens at or above a cheap lower bound of it, with the
+//      column max m and the sum z of exp(l - m) (fixed-order reductions)
+//      computed in its first two passes;
+//   2. ordered compaction: keys above the threshold, then the lowest-index
 //      tokens equal to it until C are taken;
-//   4. bitonic sort of the C unique 64-bit rank keys in LDS, descending;
-//   5. write tokens and scores exp(l - m) / z in rank order.
+//   3. the C unique 64-bit rank keys in descending order (rank sort up to
+//      128 of them, else a bitonic sort in LDS);
+//   4. write tokens and scores exp(l - m) / z in rank order.
 // ---------------------------------------------------------------------------
 constexpr int kEcThreads = 1024;
 
-__device__ inline float block_reduce_max(float v, float *sh) {
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    v = wave_max(v);
-    if (lane == 0) sh[wave] = v;
-    __syncthreads();
-    float r = sh[0];
-    for (int w = 1; w < kEcThreads / kWave; ++w) r = fmaxf(r, sh[w]);
-    __syncthreads();
-    return r;
+// Inclusive prefix sum over the 64 lanes of a wave, in lane order, on DPP
+// lane moves: shifts by 1, 2, 4 and 8 inside each row of 16 lanes, then the
+// total of rows 0 and 2 to rows 1 and 3 (row_bcast:15) and the total of
+// lanes 0..31 to rows 2 and 3 (row_bcast:31).  Lanes a move does not write
+// add 0.  (Lane exchanges through LDS take one dependent round trip per
+// step: the expert-choice bucket search took 1.4x as long with them.)
+__device__ inline int wave_incl_scan(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);   // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    return x;
 }
-__device__ inline float block_reduce_sum(float v, float *sh) {
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    v = wave_sum(v);
-    if (lane == 0) sh[wave] = v;
-    __syncthreads();
-    float r = sh[0];
-    for (int w = 1; w < kEcThreads / kWave; ++w) r += sh[w];
-    __syncthreads();
-    return r;
-}
+
 // Exclusive prefix sum over the block's threads (in thread order).
 __device__ inline int block_exclusive_scan(int v, int *sh, int *total) {
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    int incl = v;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const int n = __shfl_up(incl, o, kWave);
-        if (lane >= o) incl += n;
-    }
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
+    const int incl = wave_incl_scan(v);
     if (lane == kWave - 1) sh[wave] = incl;
     __syncthreads();
-    int base = 0, tot = 0;
-    for (int w = 0; w < kEcThreads / kWave; ++w) {
-        if (w < wave) base += sh[w];
-        tot += sh[w];
-    }
+    // the waves' totals, one per lane, scanned the same way
+    constexpr int NW = kEcThreads / kWave;
+    const int ws = wave_incl_scan(lane < NW ? sh[lane] : 0);
+    const int base = wave > 0 ? __builtin_amdgcn_readlane(ws, wave - 1) : 0;
+    *total = __builtin_amdgcn_readlane(ws, NW - 1);
     __syncthreads();
-    *total = tot;
     return base + incl - v;
 }
 
@@ -433,28 +439,35 @@ __device__ inline int block_exclusive_scan(int v, int *sh, int *total) {
 // summed in wave order.
 constexpr int kEcColMax = 16384;
 template <bool CACHE>
-__global__ __launch_bounds__(kEcThreads) void ec_select_kernel(const float *__restrict__ logits, int T, int E,
+__global__ __launch_bounds__(kEcThreads) void ec_select_kernel(const float *__restrict__ logits,
+                                                               const float *__restrict__ logits_t, int T, int E,
                                                                int C, int32_t *__restrict__ ec_idx,
                                                                float *__restrict__ ec_score, EcPermuteArgs perm) {
     constexpr int NW = kEcThreads / kWave;
     __shared__ float shf[NW];
     __shared__ int shi[NW];
-    __shared__ uint32_t hist[NW][256];
-    __shared__ uint32_t sel_prefix, sel_need;
+    __shared__ float shz[NW];
+    __shared__ uint32_t shk[NW];
+    __shared__ uint32_t hist[2][NW][256];  // per-wave histograms, two passes' worth
+    __shared__ uint32_t sel_prefix[2], sel_need[2];
     __shared__ uint64_t cand[kEcMaxCapacity];
     __shared__ float colc[CACHE ? kEcColMax : 1];
     const int e = blockIdx.x;
     const int tid = threadIdx.x, wave = tid / kWave;
-    const float *col = logits + e;
+    // the expert's column: contiguous in the transposed logits, else with
+    // stride E (each element its own cache line: the column read had been a
+    // quarter of the kernel)
+    const float *col = logits_t ? logits_t + (int64_t)e * T : logits + e;
+    const int64_t cs = logits_t ? 1 : E;
+    for (int i = tid; i < NW * 256; i += kEcThreads) hist[0][0][i] = 0;
     if constexpr (CACHE) {
-        // eight strided loads in flight per thread before their LDS stores
-        // (one at a time, each waited for, the column took most of the kernel)
+        // eight loads in flight per thread before their LDS stores
         for (int t0 = tid; t0 < T; t0 += 8 * kEcThreads) {
             float v[8];
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const int t = t0 + u * kEcThreads;
-                v[u] = t < T ? col[(int64_t)t * E] : 0.f;
+                v[u] = t < T ? col[(int64_t)t * cs] : 0.f;
             }
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
@@ -464,49 +477,117 @@ __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(const float *__re
         }
         __syncthreads();
     }
-    auto val = [&](int t) { return CACHE ? colc[t] : col[(int64_t)t * E]; };
+    auto val = [&](int t) { return CACHE ? colc[t] : col[(int64_t)t * cs]; };
+    // This thread's tokens: the contiguous chunk t0 .. t1 - 1, held in
+    // registers when the column is cached (at most kEcColMax / kEcThreads =
+    // 16 of them), so that every pass below is register arithmetic.
+    const int chunk = (T + kEcThreads - 1) / kEcThreads;
+    const int t0 = tid * chunk, t1 = min(T, t0 + chunk), nmine = max(0, t1 - t0);
+    constexpr int kMaxChunk = CACHE ? kEcColMax / kEcThreads : 1;
+    float cv[kMaxChunk];
+    if constexpr (CACHE) {
+#pragma unroll
+        for (int j = 0; j < kMaxChunk; ++j) cv[j] = j < nmine ? colc[t0 + j] : 0.f;
+    }
+    auto for_mine = [&](auto f) __attribute__((always_inline)) {
+        if constexpr (CACHE) {
+#pragma unroll
+            for (int j = 0; j < kMaxChunk; ++j)
+                if (j < nmine) f(t0 + j, cv[j]);
+        } else {
+            for (int t = t0; t < t1; ++t) f(t, val(t));
+        }
+    };
+    const int lane = tid % kWave;
+    // fixed-tree reductions over the waves' values, one per lane
+    auto waves_max = [&](const float *sh) {
+        float r = lane < NW ? sh[lane] : -INFINITY;
+#pragma unroll
+        for (int o = 1; o < NW; o <<= 1) r = fmaxf(r, __shfl_xor(r, o, kWave));
+        return __shfl(r, 0, kWave);
+    };
+    auto waves_sum = [&](const float *sh) {
+        float r = lane < NW ? sh[lane] : 0.f;
+#pragma unroll
+        for (int o = 1; o < NW; o <<= 1) r += __shfl_xor(r, o, kWave);
+        return __shfl(r, 0, kWave);
+    };
 
-    float m = -INFINITY;
-    for (int t = tid; t < T; t += kEcThreads) m = fmaxf(m, val(t));
-    m = block_reduce_max(m, shf);
-    float z = 0.f;
-    for (int t = tid; t < T; t += kEcThreads) z += expf(val(t) - m);
-    z = block_reduce_sum(z, shf);
-
+    // A lower bound of the C-th largest key when C <= NG = kEcThreads / 8:
+    // the smallest of the largest keys of NG disjoint groups of tokens (the
+    // chunks of 8 consecutive threads).  At least NG distinct tokens reach
+    // it, so the C best all do, and the radix passes count only the tokens
+    // at or above it (Gaussian logits, T = 8192, C = 128: about 6% of them).
+    // Taken on order keys, so that -0.0 and 0.0 stay apart.
+    constexpr int NG = kEcThreads / 8;
+    uint32_t floor_key = 0;
+    const bool filtered = C <= NG;
+    if (filtered) {
+        uint32_t km = 0;  // no token: the lowest key (then no filtering)
+        for_mine([&](int, float v) { km = max(km, order_key(v)); });
+#pragma unroll
+        for (int o = 1; o < 8; o <<= 1) km = max(km, (uint32_t)__shfl_xor((int)km, o, kWave));
+#pragma unroll
+        for (int o = 8; o < kWave; o <<= 1) km = min(km, (uint32_t)__shfl_xor((int)km, o, kWave));
+        if (lane == 0) shk[wave] = km;
+        __syncthreads();  // also orders the hist[0] clearing before pass 0
+        uint32_t f = lane < NW ? shk[lane] : 0xFFFFFFFFu;
+#pragma unroll
+        for (int o = 1; o < NW; o <<= 1) f = min(f, (uint32_t)__shfl_xor((int)f, o, kWave));
+        floor_key = (uint32_t)__shfl((int)f, 0, kWave);
+    } else {
+        __syncthreads();  // hist[0] cleared
+    }
+    // Radix select with two barriers per pass: the histograms of a pass are
+    // cleared during the pass before (hist[pass & 1], cleared in pass - 1
+    // or above), wave 0 alone sums the histograms and picks the bucket, and
+    // the picks alternate between two slots.  The column max m rides along
+    // in pass 0 and the sum z of exp(l - m) in pass 1 (each thread's chunk
+    // in order, then a wave reduction, then a fixed tree over the waves).
+    float m = -INFINITY, z = 0.f;
     uint32_t prefix = 0, mask = 0, need = (uint32_t)C;
     for (int pass = 0; pass < 4; ++pass) {
         const int shift = 24 - 8 * pass;
-        for (int i = tid; i < NW * 256; i += kEcThreads) (&hist[0][0])[i] = 0;
-        __syncthreads();
-        for (int t = tid; t < T; t += kEcThreads) {
-            const uint32_t u = order_key(val(t));
-            if ((u & mask) == prefix) atomicAdd(&hist[wave][(u >> shift) & 255u], 1u);
+        // filtered: few keys take part, and all waves share one histogram
+        // (row 0); else one histogram per wave (atomics contend only inside
+        // a wave), summed by wave 0
+        uint32_t(*H)[256] = hist[pass & 1];
+        uint32_t *Hw = H[filtered ? 0 : wave];
+        const int nrows = filtered ? 1 : NW;
+        uint32_t *Hn = &hist[(pass + 1) & 1][0][0];
+        for (int i = tid; i < nrows * 256; i += kEcThreads) Hn[i] = 0;
+        if (pass == 0) for_mine([&](int, float v) { m = fmaxf(m, v); });
+        if (pass == 1) for_mine([&](int, float v) { z += expf(v - m); });
+        for_mine([&](int, float v) {
+            const uint32_t u = order_key(v);
+            if (u >= floor_key && (u & mask) == prefix) atomicAdd(&Hw[(u >> shift) & 255u], 1u);
+        });
+        if (pass == 0) {
+            const float wm = wave_max(m);
+            if (lane == 0) shf[wave] = wm;
+        } else if (pass == 1) {
+            const float wz = wave_sum(z);
+            if (lane == 0) shz[wave] = wz;
         }
         __syncthreads();
-        for (int b = tid; b < 256; b += kEcThreads) {
-            uint32_t sum = 0;
-            for (int w = 0; w < NW; ++w) sum += hist[w][b];
-            hist[0][b] = sum;
-        }
-        __syncthreads();
+        if (pass == 0) m = waves_max(shf);
+        else if (pass == 1) z = waves_sum(shz);
         if (wave == 0) {
             // The bucket holding the `need`-th largest key: the first bucket,
             // from the top, whose running count reaches `need` (bucket 0 if
-            // none among 255..1 does).  Lane l takes buckets 255-4l .. 252-4l;
-            // a wave prefix sum over the lanes' totals gives the running counts.
-            const int lane = tid;
+            // none among 255..1 does).  Lane l takes buckets 255-4l .. 252-4l
+            // (summed over the histograms); a wave prefix sum over the
+            // lanes' totals gives the running counts.
             uint32_t sq[4], acc4 = 0;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                acc4 += hist[0][255 - (4 * lane + q)];
+                const int b = 255 - (4 * lane + q);
+                uint32_t hb = 0;
+                for (int w = 0; w < nrows; ++w) hb += H[w][b];
+                acc4 += hb;
                 sq[q] = acc4;
             }
-            uint32_t incl = acc4;
-#pragma unroll
-            for (int o = 1; o < kWave; o <<= 1) {
-                const uint32_t nb = __shfl_up(incl, o, kWave);
-                if (lane >= o) incl += nb;
-            }
+            const uint32_t incl = (uint32_t)wave_incl_scan((int)acc4);
             const uint32_t excl = incl - acc4;
             int qsel = -1;
 #pragma unroll
@@ -517,72 +598,73 @@ __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(const float *__re
             if (lane == winner) {
                 const int q = hit ? qsel : 3;
                 const uint32_t before = excl + (q == 0 ? 0u : q == 1 ? sq[0] : q == 2 ? sq[1] : sq[2]);
-                sel_need = need - before;
-                sel_prefix = prefix | ((uint32_t)(255 - (4 * lane + q)) << shift);
+                sel_need[pass & 1] = need - before;
+                sel_prefix[pass & 1] = prefix | ((uint32_t)(255 - (4 * lane + q)) << shift);
             }
         }
         __syncthreads();
-        need = sel_need;
-        prefix = sel_prefix;
+        need = sel_need[pass & 1];
+        prefix = sel_prefix[pass & 1];
         mask |= 255u << shift;
-        __syncthreads();
     }
     const uint32_t thr = prefix;       // order key of the C-th best token
     const int n_gt = C - (int)need;    // tokens strictly above it; `need` ties are taken
 
-    const int chunk = (T + kEcThreads - 1) / kEcThreads;
-    const int t0 = tid * chunk;
-    const int t1 = min(T, t0 + chunk);
     int gt = 0, eq = 0;
-    for (int t = t0; t < t1; ++t) {
-        const uint32_t u = order_key(val(t));
+    for_mine([&](int, float v) {
+        const uint32_t u = order_key(v);
         gt += u > thr;
         eq += u == thr;
+    });
+    // one scan for both counts, packed in 16-bit halves (every prefix is
+    // at most T, so both halves fit while T < 2^15)
+    int tot, gt_base, eq_base;
+    if (T < 32768) {
+        const int both = block_exclusive_scan((gt << 16) | eq, shi, &tot);
+        gt_base = both >> 16;
+        eq_base = both & 0xFFFF;
+    } else {
+        gt_base = block_exclusive_scan(gt, shi, &tot);
+        eq_base = block_exclusive_scan(eq, shi, &tot);
     }
-    int tot;
-    int gt_base = block_exclusive_scan(gt, shi, &tot);
-    int eq_base = block_exclusive_scan(eq, shi, &tot);
-    for (int t = t0; t < t1; ++t) {
-        const float v = val(t);
+    // (branch-free counters: incremented in branches, the compiler kept
+    // the two in a private array)
+    for_mine([&](int t, float v) {
         const uint32_t u = order_key(v);
-        if (u > thr) {
-            if (gt_base < n_gt) cand[gt_base] = rank_key(v, (uint32_t)t);
-            ++gt_base;
-        } else if (u == thr) {
-            if (eq_base < (int)need) cand[n_gt + eq_base] = rank_key(v, (uint32_t)t);
-            ++eq_base;
-        }
-    }
+        const bool g = u > thr, q = u == thr;
+        if (g && gt_base < n_gt) cand[gt_base] = rank_key(v, (uint32_t)t);
+        if (q && eq_base < (int)need) cand[n_gt + eq_base] = rank_key(v, (uint32_t)t);
+        gt_base += g;
+        eq_base += q;
+    });
     int P = 1;
     while (P < C) P <<= 1;
     if (P <= 2 * kWave) {
-        // Up to 128 candidates: wave 0 sorts them in registers, two per lane
-        // (elements lane and lane + 64), with a bitonic network of register
-        // compares and lane exchanges; zero keys pad to 128 and sort last.
+        // Up to 128 candidates with unique keys (the token index is part of
+        // the key): candidate i goes to position #(candidates with a larger
+        // key).  The threads split the comparisons: thread tid compares
+        // candidate tid % 128 with the 16 candidates 16 (tid / 128) .. + 15
+        // (broadcast LDS reads), and the 8 partial counts meet in LDS.  (A
+        // bitonic network in one wave, 28 dependent rounds of lane
+        // exchanges, took 1.6x as long.)
+        constexpr int NC = 2 * kWave, JP = NC * NC / kEcThreads;
+        static_assert(kEcThreads / NC * JP == NC, "the threads cover every pair");
+        __shared__ int rnk[NC];
+        __shared__ uint64_t srt[NC];
+        if (tid < NC) rnk[tid] = 0;
         __syncthreads();
-        if (wave == 0) {
-            const int lane = tid;
-            uint64_t v0 = lane < C ? cand[lane] : 0ull, v1 = lane + kWave < C ? cand[lane + kWave] : 0ull;
-            for (int size = 2; size <= 2 * kWave; size <<= 1) {
-                for (int stride = size >> 1; stride > 0; stride >>= 1) {
-                    if (stride == kWave) {  // partners in one lane: element lane (lower) and lane + 64
-                        const bool desc = (lane & size) == 0;
-                        const uint64_t hi = v0 > v1 ? v0 : v1, lo = v0 > v1 ? v1 : v0;
-                        v0 = desc ? hi : lo;
-                        v1 = desc ? lo : hi;
-                    } else {
-                        const uint64_t p0 = shfl_xor_u64(v0, stride), p1 = shfl_xor_u64(v1, stride);
-                        const bool lower = (lane & stride) == 0;
-                        const bool d0 = (lane & size) == 0, d1 = ((lane + kWave) & size) == 0;
-                        // the lower index keeps the larger key when descending
-                        v0 = (lower == d0) ? (v0 > p0 ? v0 : p0) : (v0 < p0 ? v0 : p0);
-                        v1 = (lower == d1) ? (v1 > p1 ? v1 : p1) : (v1 < p1 ? v1 : p1);
-                    }
-                }
-            }
-            cand[lane] = v0;
-            cand[lane + kWave] = v1;
+        const int i = tid % NC, j0 = (tid / NC) * JP;
+        if (i < C) {
+            const uint64_t ki = cand[i];
+            int c = 0;
+#pragma unroll
+            for (int j = j0; j < j0 + JP; ++j) c += j < C && cand[j] > ki;
+            atomicAdd(&rnk[i], c);
         }
+        __syncthreads();
+        if (tid < C) srt[rnk[tid]] = cand[tid];
+        __syncthreads();
+        if (tid < C) cand[tid] = srt[tid];
         __syncthreads();
     } else {
     for (int i = C + tid; i < P; i += kEcThreads) cand[i] = 0ull;
@@ -612,11 +694,13 @@ __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(const float *__re
     if (perm.slot_row == nullptr) return;
     // The permutation of expert choice: expert e owns rows e*C .. e*C + C - 1
     // in rank order; column e of slot_row is -1 except at its C tokens.
-    // The -1 fill completes (each thread's stores, then the barrier) before
-    // the rows are written over it.
-    for (int t = tid; t < T; t += kEcThreads) perm.slot_row[(int64_t)t * E + e] = -1;
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    __syncthreads();
+    // The -1 fill (unless the router wrote it, row by row) completes (each
+    // thread's stores, then the barrier) before the rows are written over it.
+    if (!perm.prefilled) {
+        for (int t = tid; t < T; t += kEcThreads) perm.slot_row[(int64_t)t * E + e] = -1;
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        __syncthreads();
+    }
     for (int j = tid; j < C; j += kEcThreads) {
         const int t = (int)rank_key_index(cand[j]);
         perm.row_token[(int64_t)e * C + j] = t;
@@ -655,11 +739,18 @@ __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(const float *__re
 // logits then meet in LDS, the bias (and softplus(x.Wn) * noise) is added in
 // a fixed order, and each wave gates whole tokens.
 // ---------------------------------------------------------------------------
+// Whether the router tile's staging buffers also hold the transposed logits
+// tile [EP][TOK] next to the logits tile [TOK][EPX] (the rows of both
+// operand buffers, 64 bf16 each, two buffers).
+constexpr bool router_tile_transposes(int TOK, int EP, int EPX) {
+    return 2 * (TOK + EPX) * 64 * 2 >= (TOK * EPX + EP * TOK) * 4;
+}
 template <int TOK, int EP, bool NOISY, int PD = 4, int NTH = 256>
 __global__ __launch_bounds__(NTH) void router_tile_kernel(
     const bf16 *__restrict__ x, const bf16 *__restrict__ wg, const float *__restrict__ bias, int T, int d, int E,
     int k, int gating, float *__restrict__ logits, int32_t *__restrict__ idx_out, float *__restrict__ w_out,
-    const bf16 *__restrict__ wn, const float *__restrict__ noise) {
+    const bf16 *__restrict__ wn, const float *__restrict__ noise, float *__restrict__ logits_t,
+    int32_t *__restrict__ fill_rows) {
     constexpr int BK = 64;
     constexpr int NW = NTH / kWave;           // waves
     constexpr int RP = NTH / 8;               // rows one pass of 16-byte chunks covers
@@ -758,6 +849,13 @@ __global__ __launch_bounds__(NTH) void router_tile_kernel(
     // float32 logits tile [TOK][EPX] in the (now free) staging buffers;
     // D[4*(lane/16) + q][lane % 16] of each 16x16 tile is acc[q]
     float *Lf = reinterpret_cast<float *>(&lds[0][0]);
+    // expert choice: the transposed tile [EP][TOK] after it, when it fits
+    // (entry tt of expert e at slot tt ^ (e % TOK), so that both the
+    // per-expert writes and the per-token reads spread over the banks)
+    float *LfT = Lf + TOK * EPX;
+    static_assert(!router_tile_transposes(TOK, EP, EPX) || 2 * ROWS * BK * 2 >= (TOK * EPX + EP * TOK) * 4,
+                  "transposed tile");
+    if (!router_tile_transposes(TOK, EP, EPX)) logits_t = nullptr;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -777,8 +875,20 @@ __global__ __launch_bounds__(NTH) void router_tile_kernel(
             if constexpr (NOISY) v += softplus(row[EP + e]) * noise[t * E + e];
             row[e] = v;
             if (logits) logits[t * E + e] = v;
+            if (logits_t) LfT[e * TOK + (tt ^ (e % TOK))] = v;
         }
         if (gating != kGateExpertChoice) gate_one_token(row, E, k, gating, t, idx_out, w_out);
+    }
+    if (logits_t) {
+        // expert choice: the transposed logits, TOK consecutive tokens of
+        // each expert, and the -1 fill of these tokens' rows of the row map
+        __syncthreads();
+        for (int i = tid; i < TOK * E; i += NTH) {
+            const int e = i / TOK, tt = i % TOK;
+            if (tok0 + tt < T) logits_t[(int64_t)e * T + tok0 + tt] = LfT[e * TOK + (tt ^ (e % TOK))];
+        }
+        for (int i = tid; i < TOK * E; i += NTH)
+            if (tok0 + i / E < T) fill_rows[tok0 * E + i] = -1;
     }
 }
 
@@ -786,29 +896,30 @@ __global__ __launch_bounds__(NTH) void router_tile_kernel(
 // host launchers
 // ---------------------------------------------------------------------------
 template <int TOK, int EP>
-static void launch_router_tile_t(const RouteArgs &a, hipStream_t s) {
+static bool launch_router_tile_t(const RouteArgs &a, hipStream_t s) {
     const int grid = (a.T + TOK - 1) / TOK;
     // register sets in flight: four, or two when a set is large (noisy, 256 experts)
     constexpr int PDN = (TOK + 2 * EP) / 32 <= 10 ? 4 : 2;
     if (a.wn)
         hipLaunchKernelGGL((router_tile_kernel<TOK, EP, true, PDN>), dim3(grid), dim3(256), 0, s, (const bf16 *)a.x,
                            (const bf16 *)a.wg, a.bias, a.T, a.d, a.E, a.k, a.gating, a.logits, a.idx, a.w,
-                           (const bf16 *)a.wn, a.noise);
+                           (const bf16 *)a.wn, a.noise, a.logits_t, a.fill_rows);
     else if constexpr (EP >= 128)  // 8 waves: 2 per SIMD (DeepSeek-style router 124 -> 109 us)
         hipLaunchKernelGGL((router_tile_kernel<TOK, EP, false, 4, 512>), dim3(grid), dim3(512), 0, s,
                            (const bf16 *)a.x, (const bf16 *)a.wg, a.bias, a.T, a.d, a.E, a.k, a.gating, a.logits,
-                           a.idx, a.w, nullptr, nullptr);
+                           a.idx, a.w, nullptr, nullptr, a.logits_t, a.fill_rows);
     else
         hipLaunchKernelGGL((router_tile_kernel<TOK, EP, false>), dim3(grid), dim3(256), 0, s, (const bf16 *)a.x,
                            (const bf16 *)a.wg, a.bias, a.T, a.d, a.E, a.k, a.gating, a.logits, a.idx, a.w,
-                           nullptr, nullptr);
+                           nullptr, nullptr, a.logits_t, a.fill_rows);
+    return a.logits_t != nullptr && router_tile_transposes(TOK, EP, a.wn ? 2 * EP : EP);
 }
 
 template <int TOK>
-static void launch_router_tile(const RouteArgs &a, hipStream_t s) {
-    if (a.E <= 64) launch_router_tile_t<TOK, 64>(a, s);
-    else if (a.E <= 128) launch_router_tile_t<TOK, 128>(a, s);
-    else launch_router_tile_t<TOK, 256>(a, s);
+static bool launch_router_tile(const RouteArgs &a, hipStream_t s) {
+    if (a.E <= 64) return launch_router_tile_t<TOK, 64>(a, s);
+    if (a.E <= 128) return launch_router_tile_t<TOK, 128>(a, s);
+    return launch_router_tile_t<TOK, 256>(a, s);
 }
 
 template <int NT, int WK>
@@ -818,15 +929,15 @@ static void launch_route_bf16_wk(const RouteArgs &a, const RoutePermuteArgs *per
         const size_t lds = (size_t)((a.T + kChunk - 1) / kChunk) * a.E * 16;
         hipLaunchKernelGGL((route_bf16_kernel<NT, WK, false, true>), dim3(1), dim3(64 * WK), lds, s,
                            (const bf16 *)a.x, (const bf16 *)a.wg, a.bias, a.T, a.d, a.E, a.k, a.gating, a.logits,
-                           a.idx, a.w, nullptr, nullptr, *perm);
+                           a.idx, a.w, nullptr, nullptr, *perm, nullptr, nullptr);
     } else if (a.wn) {
         hipLaunchKernelGGL((route_bf16_kernel<NT, WK, true>), dim3(grid), dim3(64 * WK), 0, s, (const bf16 *)a.x,
                            (const bf16 *)a.wg, a.bias, a.T, a.d, a.E, a.k, a.gating, a.logits, a.idx, a.w,
-                           (const bf16 *)a.wn, a.noise, RoutePermuteArgs{});
+                           (const bf16 *)a.wn, a.noise, RoutePermuteArgs{}, a.logits_t, a.fill_rows);
     } else {
         hipLaunchKernelGGL((route_bf16_kernel<NT, WK, false>), dim3(grid), dim3(64 * WK), 0, s, (const bf16 *)a.x,
                            (const bf16 *)a.wg, a.bias, a.T, a.d, a.E, a.k, a.gating, a.logits, a.idx, a.w,
-                           nullptr, nullptr, RoutePermuteArgs{});
+                           nullptr, nullptr, RoutePermuteArgs{}, a.logits_t, a.fill_rows);
     }
 }
 
@@ -847,24 +958,24 @@ void launch_route_permute(const RouteArgs &a, const RoutePermuteArgs &p, hipStre
     launch_route_bf16_t<1>(a, s, &p);
 }
 
-void launch_route(const RouteArgs &a, hipStream_t s) {
-    if (a.T == 0) return;
+bool launch_route(const RouteArgs &a, hipStream_t s) {
+    if (a.T == 0) return false;
     if (!a.bf16) {
         hipLaunchKernelGGL(route_f32_kernel, dim3((a.T + 3) / 4), dim3(256), 0, s, (const float *)a.x,
                            (const float *)a.wg, a.bias, a.T, a.d, a.E, a.k, a.gating, a.logits, a.idx, a.w,
                            (const float *)a.wn, a.noise);
-        return;
+        return false;
     }
     // Up to 16 experts: per-wave K slices straight from global memory.  More
     // experts: LDS-staged tiles, so that a block's tokens share each weight
     // row instead of every 16-token wave re-reading all of them from L2.
     if (a.E <= 16) {
         launch_route_bf16_t<1>(a, s);
-        return;
+        return a.logits_t != nullptr;
     }
     // 32-token blocks unless that already gives a block per CU twice over
-    if (a.T >= 64 * 512) launch_router_tile<64>(a, s);
-    else launch_router_tile<32>(a, s);
+    if (a.T >= 64 * 512) return launch_router_tile<64>(a, s);
+    return launch_router_tile<32>(a, s);
 }
 
 void launch_gate_logits(const float *logits, int T, int E, int k, int gating, int32_t *idx, float *w,
@@ -874,14 +985,14 @@ void launch_gate_logits(const float *logits, int T, int E, int k, int gating, in
 }
 
 void launch_ec_select(const float *logits, int T, int E, int C, int32_t *ec_idx, float *ec_score,
-                      hipStream_t s, const EcPermuteArgs *perm) {
+                      hipStream_t s, const EcPermuteArgs *perm, const float *logits_t) {
     const EcPermuteArgs pa = perm ? *perm : EcPermuteArgs{};
     if (T <= kEcColMax)
-        hipLaunchKernelGGL(ec_select_kernel<true>, dim3(E), dim3(kEcThreads), 0, s, logits, T, E, C, ec_idx, ec_score,
-                           pa);
-    else
-        hipLaunchKernelGGL(ec_select_kernel<false>, dim3(E), dim3(kEcThreads), 0, s, logits, T, E, C, ec_idx,
+        hipLaunchKernelGGL(ec_select_kernel<true>, dim3(E), dim3(kEcThreads), 0, s, logits, logits_t, T, E, C, ec_idx,
                            ec_score, pa);
+    else
+        hipLaunchKernelGGL(ec_select_kernel<false>, dim3(E), dim3(kEcThreads), 0, s, logits, logits_t, T, E, C,
+                           ec_idx, ec_score, pa);
 }
 
 }  // namespace moe
