@@ -63,6 +63,23 @@ __device__ inline uint64_t wave_max_u64(uint64_t v) {
     return v;
 }
 // Butterfly sum: every lane ends with the same value, in a fixed order.
+// Inclusive prefix sum over the 64 lanes of a wave, in lane order, on DPP
+// lane moves: shifts by 1, 2, 4 and 8 inside each row of 16 lanes, then the
+// total of rows 0 and 2 to rows 1 and 3 (row_bcast:15) and the total of
+// lanes 0..31 to rows 2 and 3 (row_bcast:31).  Lanes a move does not write
+// add 0.  All 64 lanes must be active.  (Lane exchanges through LDS take
+// one dependent round trip per step: the expert-choice bucket search took
+// 1.4x as long with them.)
+__device__ inline int wave_incl_scan(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);   // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    return x;
+}
+
 __device__ inline float wave_sum(float v) {
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);

@@ -45,21 +45,13 @@ __device__ void permute_small_block(const int32_t *__restrict__ idx, int T, int 
     //   pre(c) = P(c) - cnt(c) - P(first chunk of c's group - 1)  (into pre)
     //   base(c) = kept assignments to e in chunks before c      (into base)
     __shared__ int ktot[kMaxSmallExperts];
-    auto wave_incl = [&](int v) {
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-            const int n = __shfl_up(v, o, kWave);
-            if (lane >= o) v += n;
-        }
-        return v;
-    };
     for (int e = wave; e < E; e += NTH / kWave) {
         int carry = 0;
         for (int c0 = 0; c0 < nc; c0 += kWave) {
             const int c = c0 + lane;
-            const int incl = wave_incl(c < nc ? __popcll(masks[c * E + e]) : 0);
+            const int incl = wave_incl_scan(c < nc ? __popcll(masks[c * E + e]) : 0);
             if (c < nc) base[c * E + e] = carry + incl;
-            carry += __shfl(incl, kWave - 1, kWave);
+            carry += __builtin_amdgcn_readlane(incl, kWave - 1);
         }
         for (int c0 = 0; c0 < nc; c0 += kWave) {
             const int c = c0 + lane;
@@ -80,9 +72,9 @@ __device__ void permute_small_block(const int32_t *__restrict__ idx, int T, int 
                     kept = room <= 0 ? 0 : (room < cnt ? room : cnt);
                 }
             }
-            const int incl = wave_incl(kept);
+            const int incl = wave_incl_scan(kept);
             if (c < nc) base[c * E + e] = carry + incl - kept;
-            carry += __shfl(incl, kWave - 1, kWave);
+            carry += __builtin_amdgcn_readlane(incl, kWave - 1);
         }
         if (lane == 0) {
             ktot[e] = carry;
@@ -92,12 +84,7 @@ __device__ void permute_small_block(const int32_t *__restrict__ idx, int T, int 
     __syncthreads();
     const int kept_total = tid < E ? ktot[tid] : 0;
     // exclusive scan of the kept counts over experts (thread order)
-    int incl = kept_total;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const int n = __shfl_up(incl, o, kWave);
-        if (lane >= o) incl += n;
-    }
+    const int incl = wave_incl_scan(kept_total);
     if (lane == kWave - 1) wsum[wave] = incl;
     __syncthreads();
     int before = 0, total = 0;

@@ -102,12 +102,7 @@ __global__ __launch_bounds__(kScanThreads) void permute_scan_kernel(int nc, int 
     }
     // exclusive scan of counts over experts (thread order == expert order)
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    int incl = kept_total;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const int n = __shfl_up(incl, o, kWave);
-        if (lane >= o) incl += n;
-    }
+    const int incl = wave_incl_scan(kept_total);
     if (lane == kWave - 1) wsum[wave] = incl;
     __syncthreads();
     int base = 0, total = 0;

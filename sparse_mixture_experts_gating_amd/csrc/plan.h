@@ -40,26 +40,16 @@ __device__ inline void build_tile_plan(const int32_t *counts, const int32_t *off
             const int c = e < E ? counts[e] : 0;
             const int v = (c + BM - 1) / BM;
             const int hv = c >= BM ? v : 0, lv = c > 0 && c < BM ? 1 : 0;
-            int incl = v, hincl = hv, lincl = lv;
-#pragma unroll
-            for (int o = 1; o < kWave; o <<= 1) {
-                const int n = __shfl_up(incl, o, kWave), hn = __shfl_up(hincl, o, kWave);
-                const int ln = __shfl_up(lincl, o, kWave);
-                if (lane >= o) {
-                    incl += n;
-                    hincl += hn;
-                    lincl += ln;
-                }
-            }
+            const int incl = wave_incl_scan(v), hincl = wave_incl_scan(hv), lincl = wave_incl_scan(lv);
             if (e < E) {
                 mstart[e] = base + incl - v;
                 ms[e] = base + incl - v;
                 hs[e] = hbase + hincl - hv;
                 ls[e] = lbase + lincl - lv;
             }
-            base += __shfl(incl, kWave - 1, kWave);
-            hbase += __shfl(hincl, kWave - 1, kWave);
-            lbase += __shfl(lincl, kWave - 1, kWave);
+            base += __builtin_amdgcn_readlane(incl, kWave - 1);
+            hbase += __builtin_amdgcn_readlane(hincl, kWave - 1);
+            lbase += __builtin_amdgcn_readlane(lincl, kWave - 1);
         }
         if (lane == 0) {
             mstart[E] = base;

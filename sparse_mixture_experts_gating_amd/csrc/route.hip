@@ -402,22 +402,6 @@ void launch_router_stats(const float *logits, const int32_t *idx, int T, int E, 
 // ---------------------------------------------------------------------------
 constexpr int kEcThreads = 1024;
 
-// Inclusive prefix sum over the 64 lanes of a wave, in lane order, on DPP
-// lane moves: shifts by 1, 2, 4 and 8 inside each row of 16 lanes, then the
-// total of rows 0 and 2 to rows 1 and 3 (row_bcast:15) and the total of
-// lanes 0..31 to rows 2 and 3 (row_bcast:31).  Lanes a move does not write
-// add 0.  (Lane exchanges through LDS take one dependent round trip per
-// step: the expert-choice bucket search took 1.4x as long with them.)
-__device__ inline int wave_incl_scan(int x) {
-    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1
-    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
-    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);   // row_shr:4
-    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);   // row_shr:8
-    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
-    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
-    return x;
-}
-
 // Exclusive prefix sum over the block's threads (in thread order).
 __device__ inline int block_exclusive_scan(int v, int *sh, int *total) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
