@@ -157,7 +157,7 @@ struct GemmArgs {
     // (s+1) * kslice - 1 of the K axis; 0 = B is [G][N][K].
     int kslice = 0;
 };
-enum GemmShape { kGemmPrefill = 0, kGemmSmallM = 1, kGemmDecode = 2 };
+enum GemmShape { kGemmPrefill = 0, kGemmSmallM = 1, kGemmDecode = 2, kGemmMid = 3 };
 // Router logits of many experts as a dense GEMM: x [T][d] times wg [E][d]^T
 // (E <= 256), split into S K parts whose float32 sums go to partout [S][T][E];
 // launch_gate_partials adds them up and gates.

@@ -382,16 +382,19 @@ int pick_shape(const Derived &D) {
     if (avg <= 160.0 || max_rows <= 384) {
         // When even the 128-row tiles of the down projection (N = d, 256
         // columns a tile) cannot fill the CUs, each tile's K loop is the
-        // critical path and 32-row tiles spread the work over more CUs, as
+        // critical path and smaller tiles spread the work over more CUs, as
         // long as the extra m-tiles do not re-stream weights from HBM: few
-        // rows per expert (one 32-row tile each) or weights that stay in the
-        // 256 MB MALL.  Measured: Switch layer 0.085 -> 0.061 ms; Mixtral
-        // shape T = 64 0.67 -> 0.60 ms, but T = 128 and 256 faster on 128-row
-        // tiles (0.69 vs 0.73, 0.69 vs 0.76 ms).
+        // rows per expert (32-row tiles, one each) or weights that stay in
+        // the 256 MB MALL (64-row tiles, half the weight re-reads of 32-row
+        // ones).  Measured: Switch layer 0.085 -> 0.061 ms on 32-row tiles,
+        // then 0.070 -> 0.063 ms on 64-row ones (alternating runs); Mixtral
+        // shape T = 64 0.67 -> 0.60 ms on 32-row tiles, but T = 128 and 256
+        // faster on 128-row tiles (0.69 vs 0.73, 0.69 vs 0.76 ms).
         const int64_t tiles = ((kept_max + 127) / 128 + D.E) * ((D.d + 255) / 256);
         const double wbytes = (double)D.E * D.F * D.d * D.elem * (D.act == MOE_ACT_SWIGLU ? 3 : 2);
         const bool few_rows = avg <= 24.0, cached = wbytes <= 128e6;
-        return tiles < device_cus() && (few_rows || cached) ? kGemmDecode : kGemmSmallM;
+        if (tiles < device_cus() && few_rows) return kGemmDecode;
+        return tiles < device_cus() && cached ? kGemmMid : kGemmSmallM;
     }
     return kGemmPrefill;
 }
