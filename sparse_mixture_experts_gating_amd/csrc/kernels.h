@@ -59,10 +59,15 @@ struct PermuteArgs {
     int32_t *counts, *offsets, *row_token, *slot_row;
 };
 // One-workgroup permutation (count, scan and scatter in LDS) for batches whose
-// chunk tables fit: E <= kMaxSmallExperts, nc * E * 16 <= kSmallLdsBytes and
+// chunk tables fit: E <= kMaxSmallExperts, small_tables_bytes(T, E) <= kSmallLdsBytes and
 // T * k <= kSmallMaxSlots.  Writes counts, offsets, row_token and slot_row.
 constexpr int kMaxSmallExperts = 1024;
 constexpr int kSmallLdsBytes = 40 * 1024;
+// LDS of the one-workgroup permutation's chunk tables: masks (8 bytes),
+// prefixes and bases (4 bytes each) of nc = ceil(T / 64) chunks, in rows of
+// E + 1 entries (the padding entry spreads one expert's column over the LDS
+// banks: with rows of E = 16 the masks of a column shared two banks)
+inline int64_t small_tables_bytes(int64_t T, int E) { return (T + kChunk - 1) / kChunk * (E + 1) * 16; }
 constexpr int kSmallMaxSlots = 16384;
 bool permute_small_fits(int T, int E, int k);
 // The grouped GEMMs' tile plan (see launch_tile_plan), built at the end of

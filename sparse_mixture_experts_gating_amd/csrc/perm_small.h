@@ -10,8 +10,10 @@
 namespace moe {
 
 // Run by all NTH threads of one workgroup.  idx [T][k] may have been written
-// by this workgroup before a barrier.  lds_u64: 16 nc E bytes of LDS, nc =
-// ceil(T / kChunk) token chunks.  Writes counts [E], offsets [E + 1],
+// by this workgroup before a barrier.  lds_u64: small_tables_bytes(T, E)
+// bytes of LDS: three tables of nc = ceil(T / kChunk) token-chunk rows of
+// ES = E + 1 entries (the padding entry keeps one expert's column off a
+// single LDS bank).  Writes counts [E], offsets [E + 1],
 // row_token and slot_row [T][k] (-1: dropped) and, when plan.mstart is set,
 // the grouped GEMMs' tile plan.  The layout and its order are those of the
 // count / scan / scatter kernels: each expert's rows in ascending token
@@ -21,23 +23,35 @@ __device__ void permute_small_block(const int32_t *__restrict__ idx, int T, int 
                                     int group_chunks, int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
                                     int32_t *__restrict__ row_token, int32_t *__restrict__ slot_row,
                                     const TilePlanArgs &plan, unsigned long long *lds_u64) {
-    const int nc = (T + kChunk - 1) / kChunk;
-    unsigned long long *masks = lds_u64;                   // [nc][E]
-    int32_t *pre = (int32_t *)(masks + (int64_t)nc * E);  // [nc][E] in-group prefix before the chunk
-    int32_t *base = pre + (int64_t)nc * E;                  // [nc][E] kept rows of e before the chunk
+    const int nc = (T + kChunk - 1) / kChunk, ES = E + 1;
+    unsigned long long *masks = lds_u64;                    // [nc][ES]
+    int32_t *pre = (int32_t *)(masks + (int64_t)nc * ES);  // [nc][ES] in-group prefix before the chunk
+    int32_t *base = pre + (int64_t)nc * ES;                  // [nc][ES] kept rows of e before the chunk
     __shared__ int wsum[NTH / kWave];
     __shared__ int offs[kMaxSmallExperts + 1];
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-    for (int i = tid; i < nc * E; i += NTH) masks[i] = 0ull;
+    for (int i = tid; i < nc * ES; i += NTH) masks[i] = 0ull;
     __syncthreads();
-    // chunk masks: bit l of masks[c][e] = token 64c + l chose e
-    for (int c = wave; c < nc; c += NTH / kWave) {
-        const int t = c * kChunk + lane;
-        if (t < T)
-            for (int j = 0; j < k; ++j) {
-                const int e = idx[(int64_t)t * k + j];
-                if (e >= 0 && e < E) atomicOr(&masks[c * E + e], 1ull << lane);
-            }
+    // chunk masks: bit l of masks[c][e] = token 64c + l chose e.  Wave w
+    // takes chunks w, w + NW, ...; each lane issues up to kLoads of its
+    // (chunk, slot) idx loads before the first atomic, so the phase waits
+    // for about one load latency instead of one per chunk.
+    constexpr int NW = NTH / kWave, kLoads = 8;
+    const int n = T * k;  // <= kSmallMaxSlots
+    const int npairs = (nc > wave ? (nc - wave + NW - 1) / NW : 0) * k;
+    for (int p0 = 0; p0 < npairs; p0 += kLoads) {
+        int ev[kLoads];
+#pragma unroll
+        for (int u = 0; u < kLoads; ++u) {
+            const int p = p0 + u, q = p / k, j = p - q * k;
+            const int t = (wave + q * NW) * kChunk + lane;
+            ev[u] = p < npairs && t < T ? idx[t * k + j] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < kLoads; ++u) {
+            const int c = wave + ((p0 + u) / k) * NW, e = ev[u];
+            if (e >= 0 && e < E) atomicOr(&masks[c * ES + e], 1ull << lane);
+        }
     }
     __syncthreads();
     // per expert, one wave: wave-wide scans over windows of 64 chunks give
@@ -49,15 +63,16 @@ __device__ void permute_small_block(const int32_t *__restrict__ idx, int T, int 
         int carry = 0;
         for (int c0 = 0; c0 < nc; c0 += kWave) {
             const int c = c0 + lane;
-            const int incl = wave_incl_scan(c < nc ? __popcll(masks[c * E + e]) : 0);
-            if (c < nc) base[c * E + e] = carry + incl;
+            const int incl = wave_incl_scan(c < nc ? __popcll(masks[c * ES + e]) : 0);
+            if (c < nc) base[c * ES + e] = carry + incl;
             carry += __builtin_amdgcn_readlane(incl, kWave - 1);
         }
         for (int c0 = 0; c0 < nc; c0 += kWave) {
             const int c = c0 + lane;
             if (c < nc) {
                 const int head = group_chunks > 0 ? c - c % group_chunks : 0;
-                pre[c * E + e] = base[c * E + e] - __popcll(masks[c * E + e]) - (head > 0 ? base[(head - 1) * E + e] : 0);
+                pre[c * ES + e] =
+                    base[c * ES + e] - __popcll(masks[c * ES + e]) - (head > 0 ? base[(head - 1) * ES + e] : 0);
             }
         }
         carry = 0;
@@ -65,15 +80,15 @@ __device__ void permute_small_block(const int32_t *__restrict__ idx, int T, int 
             const int c = c0 + lane;
             int kept = 0;
             if (c < nc) {
-                const int cnt = __popcll(masks[c * E + e]);
+                const int cnt = __popcll(masks[c * ES + e]);
                 kept = cnt;
                 if (capacity > 0) {
-                    const int room = capacity - pre[c * E + e];
+                    const int room = capacity - pre[c * ES + e];
                     kept = room <= 0 ? 0 : (room < cnt ? room : cnt);
                 }
             }
             const int incl = wave_incl_scan(kept);
-            if (c < nc) base[c * E + e] = carry + incl - kept;
+            if (c < nc) base[c * ES + e] = carry + incl - kept;
             carry += __builtin_amdgcn_readlane(incl, kWave - 1);
         }
         if (lane == 0) {
@@ -87,11 +102,11 @@ __device__ void permute_small_block(const int32_t *__restrict__ idx, int T, int 
     const int incl = wave_incl_scan(kept_total);
     if (lane == kWave - 1) wsum[wave] = incl;
     __syncthreads();
-    int before = 0, total = 0;
-    for (int w = 0; w < NTH / kWave; ++w) {
-        if (w < wave) before += wsum[w];
-        total += wsum[w];
-    }
+    // the waves' totals, one per lane, scanned the same way
+    const int ws = wave_incl_scan(lane < NW ? wsum[lane] : 0);
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const int before = wv > 0 ? __builtin_amdgcn_readlane(ws, wv - 1) : 0;
+    const int total = __builtin_amdgcn_readlane(ws, NW - 1);
     if (tid < E) {
         offs[tid] = before + incl - kept_total;
         offsets[tid] = before + incl - kept_total;
@@ -102,23 +117,30 @@ __device__ void permute_small_block(const int32_t *__restrict__ idx, int T, int 
     }
     __syncthreads();
     // rows: offsets[e] + base + rank inside the chunk, or -1 past the capacity
-    const int64_t n = (int64_t)T * k;
-    for (int64_t i = tid; i < n; i += NTH) {
-        const int t = (int)(i / k);
-        const int e = idx[i];
-        if (e < 0 || e >= E) {
-            slot_row[i] = -1;
-            continue;
+    // (kLoads idx loads in flight per thread, as above)
+    for (int i0 = tid; i0 < n; i0 += kLoads * NTH) {
+        int ev[kLoads];
+#pragma unroll
+        for (int u = 0; u < kLoads; ++u) {
+            const int i = i0 + u * NTH;
+            ev[u] = i < n ? idx[i] : -1;
         }
-        const int ce = (t / kChunk) * E + e;
-        const int r = __popcll(masks[ce] & ((1ull << (t % kChunk)) - 1ull));
-        if (capacity > 0 && pre[ce] + r >= capacity) {
-            slot_row[i] = -1;
-            continue;
+#pragma unroll
+        for (int u = 0; u < kLoads; ++u) {
+            const int i = i0 + u * NTH, e = ev[u];
+            if (i >= n) break;
+            int row = -1;
+            if (e >= 0 && e < E) {
+                const int t = i / k;
+                const int ce = (t / kChunk) * ES + e;
+                const int r = __popcll(masks[ce] & ((1ull << (t % kChunk)) - 1ull));
+                if (capacity <= 0 || pre[ce] + r < capacity) {
+                    row = offs[e] + base[ce] + r;
+                    row_token[row] = t;
+                }
+            }
+            slot_row[i] = row;
         }
-        const int row = offs[e] + base[ce] + r;
-        slot_row[i] = row;
-        row_token[row] = t;
     }
     if (plan.mstart != nullptr) {
         __shared__ int plan_scratch[3 * (kMaxSmallExperts + 1)];

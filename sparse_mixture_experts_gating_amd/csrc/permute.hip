@@ -162,14 +162,13 @@ __global__ __launch_bounds__(kSmallThreads) void permute_small_kernel(const int3
 }
 
 bool permute_small_fits(int T, int E, int k) {
-    const int64_t nc = ((int64_t)T + kChunk - 1) / kChunk;
-    return E <= kMaxSmallExperts && nc * E * 16 <= kSmallLdsBytes && (int64_t)T * k <= kSmallMaxSlots;
+    return E <= kMaxSmallExperts && small_tables_bytes(T, E) <= kSmallLdsBytes && (int64_t)T * k <= kSmallMaxSlots;
 }
 
 void launch_permute_small(const PermuteArgs &a, const TilePlanArgs &plan, hipStream_t s) {
-    const int64_t nc = ((int64_t)a.T + kChunk - 1) / kChunk;
-    hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(kSmallThreads), (size_t)(nc * a.E * 16), s, a.idx, a.T,
-                       a.E, a.k, a.capacity, a.group_chunks, a.counts, a.offsets, a.row_token, a.slot_row, plan);
+    hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(kSmallThreads), (size_t)small_tables_bytes(a.T, a.E), s,
+                       a.idx, a.T, a.E, a.k, a.capacity, a.group_chunks, a.counts, a.offsets, a.row_token, a.slot_row,
+                       plan);
 }
 
 void launch_permute_count(const PermuteArgs &a, hipStream_t s) {

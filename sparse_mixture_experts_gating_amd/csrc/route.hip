@@ -910,7 +910,7 @@ template <int NT, int WK>
 static void launch_route_bf16_wk(const RouteArgs &a, const RoutePermuteArgs *perm, hipStream_t s) {
     const int grid = (a.T + 15) / 16;
     if (perm) {  // one block (route_permute_fits): route, then permute in the same block
-        const size_t lds = (size_t)((a.T + kChunk - 1) / kChunk) * a.E * 16;
+        const size_t lds = (size_t)small_tables_bytes(a.T, a.E);
         hipLaunchKernelGGL((route_bf16_kernel<NT, WK, false, true>), dim3(1), dim3(64 * WK), lds, s,
                            (const bf16 *)a.x, (const bf16 *)a.wg, a.bias, a.T, a.d, a.E, a.k, a.gating, a.logits,
                            a.idx, a.w, nullptr, nullptr, *perm, nullptr, nullptr);

@@ -131,14 +131,15 @@ def test_fused_route_bit_exact_on_exact_inputs(spec):
 PERM_CASES = [  # T, E, k, capacity_factor, group
     (777, 8, 2, 0.0, 0), (4096, 16, 1, 1.25, 1024), (8192, 256, 8, 0.0, 0), (640, 16, 1, 1.25, 320),
     (1000, 16, 1, 1.25, 0), (130, 64, 6, 0.0, 0), (64, 1, 1, 0.0, 0), (1, 4, 4, 0.0, 0),
-    # at and past the limits of the one-workgroup path (T*k <= 16384, chunk tables <= 40 KiB)
-    (16384, 8, 1, 0.0, 0), (1280, 128, 2, 0.0, 0), (1344, 128, 2, 0.0, 0), (20000, 16, 1, 1.25, 1024),
-    (3000, 64, 6, 0.0, 0)]
+    # at and past the limits of the one-workgroup path (T*k <= 16384; chunk tables of nc = ceil(T / 64)
+    # rows of E + 1 entries, 16 bytes each, <= 40 KiB)
+    (16384, 8, 1, 0.0, 0), (1280, 127, 2, 0.0, 0), (1280, 128, 2, 0.0, 0), (1344, 128, 2, 0.0, 0),
+    (20000, 16, 1, 1.25, 1024), (3000, 64, 6, 0.0, 0)]
 
 
 def _small_path(T, E, k):
     nc = (T + 63) // 64
-    return T * k <= 16384 and nc * E * 16 <= 40 * 1024
+    return T * k <= 16384 and nc * (E + 1) * 16 <= 40 * 1024
 
 
 @pytest.mark.parametrize("T,E,k,cf,group", PERM_CASES)
