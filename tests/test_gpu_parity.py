@@ -134,7 +134,9 @@ PERM_CASES = [  # T, E, k, capacity_factor, group
     # at and past the limits of the one-workgroup path (T*k <= 16384; chunk tables of nc = ceil(T / 64)
     # rows of E + 1 entries, 16 bytes each, <= 40 KiB)
     (16384, 8, 1, 0.0, 0), (1280, 127, 2, 0.0, 0), (1280, 128, 2, 0.0, 0), (1344, 128, 2, 0.0, 0),
-    (20000, 16, 1, 1.25, 1024), (3000, 64, 6, 0.0, 0)]
+    (20000, 16, 1, 1.25, 1024), (3000, 64, 6, 0.0, 0),
+    # the most experts the permutation accepts (1024): one-workgroup path, three-kernel path, capacity drops
+    (100, 1024, 4, 0.0, 0), (3000, 1024, 2, 0.0, 0), (4096, 1024, 1, 1.25, 1024)]
 
 
 def _small_path(T, E, k):
