@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace moe {
@@ -49,46 +51,70 @@ __device__ inline uint64_t rank_key(float v, uint32_t idx) {
 }
 __device__ inline uint32_t rank_key_index(uint64_t key) { return ~(uint32_t)(key & 0xffffffffu); }
 
-__device__ inline uint64_t shfl_xor_u64(uint64_t v, int mask) {
-    uint32_t lo = __shfl_xor((uint32_t)v, mask, kWave);
-    uint32_t hi = __shfl_xor((uint32_t)(v >> 32), mask, kWave);
-    return ((uint64_t)hi << 32) | lo;
+// Wave reductions on DPP lane moves (all 64 lanes must be active): an
+// inclusive scan inside each row of 16 lanes (row_shr by 1, 2, 4 and 8),
+// then row 0's and row 2's results to rows 1 and 3 (row_bcast:15) and lanes
+// 0..31's result to rows 2 and 3 (row_bcast:31), so lane 63 ends with the
+// whole wave's; every lane then reads lane 63.  Lanes a move does not write
+// see the identity (0, or -inf for the float maximum).  The order of the
+// float sum is fixed.  (Through LDS lane exchanges, one dependent round
+// trip per step, the gating of one token took several times as long.)
+template <int CTRL, int ROWS, bool BOUND>
+__device__ inline uint32_t dpp_u32(uint32_t v, uint32_t identity) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)identity, (int)v, CTRL, ROWS, 0xf, BOUND);
+}
+template <int CTRL, int ROWS, bool BOUND>
+__device__ inline float dpp_f32(float v, float identity) {
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(__float_as_int(identity), __float_as_int(v), CTRL, ROWS, 0xf, BOUND));
 }
 __device__ inline uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-        uint64_t o = shfl_xor_u64(v, m);
-        v = o > v ? o : v;
-    }
-    return v;
+    auto step = [](uint64_t x, uint64_t o) { return o > x ? o : x; };
+    auto mv = [](uint64_t x, auto ctrl) {
+        constexpr int C = decltype(ctrl)::value;
+        constexpr int R = C == 0x142 ? 0xa : C == 0x143 ? 0xc : 0xf;
+        constexpr bool B = C < 0x140;
+        const uint32_t lo = dpp_u32<C, R, B>((uint32_t)x, 0u), hi = dpp_u32<C, R, B>((uint32_t)(x >> 32), 0u);
+        return ((uint64_t)hi << 32) | lo;
+    };
+    v = step(v, mv(v, std::integral_constant<int, 0x111>{}));
+    v = step(v, mv(v, std::integral_constant<int, 0x112>{}));
+    v = step(v, mv(v, std::integral_constant<int, 0x114>{}));
+    v = step(v, mv(v, std::integral_constant<int, 0x118>{}));
+    v = step(v, mv(v, std::integral_constant<int, 0x142>{}));
+    v = step(v, mv(v, std::integral_constant<int, 0x143>{}));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+    return ((uint64_t)hi << 32) | lo;
 }
-// Butterfly sum: every lane ends with the same value, in a fixed order.
-// Inclusive prefix sum over the 64 lanes of a wave, in lane order, on DPP
-// lane moves: shifts by 1, 2, 4 and 8 inside each row of 16 lanes, then the
-// total of rows 0 and 2 to rows 1 and 3 (row_bcast:15) and the total of
-// lanes 0..31 to rows 2 and 3 (row_bcast:31).  Lanes a move does not write
-// add 0.  All 64 lanes must be active.  (Lane exchanges through LDS take
-// one dependent round trip per step: the expert-choice bucket search took
-// 1.4x as long with them.)
+// Inclusive prefix sum over the 64 lanes of a wave, in lane order (the
+// same DPP moves; lane 63 holds the total).
 __device__ inline int wave_incl_scan(int x) {
-    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1
-    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
-    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);   // row_shr:4
-    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);   // row_shr:8
-    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
-    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    x += (int)dpp_u32<0x111, 0xf, true>((uint32_t)x, 0u);   // row_shr:1
+    x += (int)dpp_u32<0x112, 0xf, true>((uint32_t)x, 0u);   // row_shr:2
+    x += (int)dpp_u32<0x114, 0xf, true>((uint32_t)x, 0u);   // row_shr:4
+    x += (int)dpp_u32<0x118, 0xf, true>((uint32_t)x, 0u);   // row_shr:8
+    x += (int)dpp_u32<0x142, 0xa, false>((uint32_t)x, 0u);  // row_bcast:15
+    x += (int)dpp_u32<0x143, 0xc, false>((uint32_t)x, 0u);  // row_bcast:31
     return x;
 }
-
 __device__ inline float wave_sum(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
-    return v;
+    v += dpp_f32<0x111, 0xf, true>(v, 0.f);
+    v += dpp_f32<0x112, 0xf, true>(v, 0.f);
+    v += dpp_f32<0x114, 0xf, true>(v, 0.f);
+    v += dpp_f32<0x118, 0xf, true>(v, 0.f);
+    v += dpp_f32<0x142, 0xa, false>(v, 0.f);
+    v += dpp_f32<0x143, 0xc, false>(v, 0.f);
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 __device__ inline float wave_max(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
-    return v;
+    v = fmaxf(v, dpp_f32<0x111, 0xf, false>(v, -INFINITY));
+    v = fmaxf(v, dpp_f32<0x112, 0xf, false>(v, -INFINITY));
+    v = fmaxf(v, dpp_f32<0x114, 0xf, false>(v, -INFINITY));
+    v = fmaxf(v, dpp_f32<0x118, 0xf, false>(v, -INFINITY));
+    v = fmaxf(v, dpp_f32<0x142, 0xa, false>(v, -INFINITY));
+    v = fmaxf(v, dpp_f32<0x143, 0xc, false>(v, -INFINITY));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 __device__ inline float silu(float z) { return z / (1.0f + expf(-z)); }
