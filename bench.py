@@ -289,6 +289,14 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
 
+    # measured HBM rates: context for the HBM-bound kernels (the roofline
+    # peak stays the published figure)
+    with torch.cuda.stream(stream):
+        hbm = measured_bandwidth(torch, dev, stream)
+    for v in kern.values():
+        if v["unit"] == "GB/s":
+            v["frac_of_measured_read"] = round(v["achieved"] / hbm["read_gbps"], 4)
+
     cpu = parity = None
     if not args.no_cpu_baseline:
         cpu, parity = cpu_baseline(spec, inp, args.cpu_seconds, y, routing)
@@ -325,11 +333,46 @@ def main():
         "kernels_cold_us": kern_cold,
         "kernels": kern,
         "roofline": roofline,
+        "hbm_measured": hbm,
         "routing": routing_summary(spec, counts),
         "parity": parity,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def measured_bandwidth(torch, dev, stream, mib=1024, reps=5):
+    """HBM rates of plain torch kernels on this GPU, for context next to the
+    published 8 TB/s: a device copy of `mib` MiB (bytes read + written per
+    second) and a read-only pass over `mib` MiB (float32 row sums of a
+    [n / 4096][4096] view; of torch's reductions the fastest reader, a plain
+    sum of the flat tensor reads at about two thirds of its rate).
+    Event-timed on the launch stream, median of `reps`."""
+    import numpy as np
+    n = mib << 20
+    src = torch.empty(n // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+
+    def timed(f):
+        f()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            f()
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) / 1e3)
+        return float(np.median(ts))
+
+    t_copy = timed(lambda: dst.copy_(src))
+    rows = src.view(-1, 4096)
+    t_read = timed(lambda: rows.sum(dim=1))
+    del src, dst
+    return {"copy_gbps": round(2 * n / t_copy / 1e9, 1), "read_gbps": round(n / t_read / 1e9, 1), "mib": mib,
+            "how": "torch device copy, and float32 row sums of a [n/4096][4096] view, of 1 GiB; "
+                   "event-timed, median of 5"}
 
 
 def routing_summary(spec, counts):
