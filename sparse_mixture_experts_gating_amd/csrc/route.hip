@@ -80,6 +80,71 @@ __device__ void gate_one_token(const float *row, int E, int k, int gating, int64
     }
 }
 
+// One lane gates one token of E <= EMAX <= kLaneGateMax experts (logits at
+// `row`, in LDS or global memory), with the selection and weights of
+// gate_one_token: slot j takes the largest logit not taken by slots 0..j-1
+// (order_key; the lowest index among equal keys), so the slots come out in
+// rank order; the softmax sums run in slot order (topk-softmax) or expert
+// order (softmax-topk, switch).  For few experts a wave gates up to 64
+// tokens this way in fewer instructions than the wave-wide selection (DPP
+// maxima of 64-bit keys) takes for one.
+constexpr int kLaneGateMax = 16;
+template <int EMAX>
+__device__ __forceinline__ void gate_token_lane(const float *row, int E, int k, int gating, int64_t t,
+                                       int32_t *__restrict__ idx_out, float *__restrict__ w_out) {
+    static_assert(EMAX <= kLaneGateMax, "experts of one lane");
+    float v[EMAX];
+    uint32_t key[EMAX];
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e) {
+        v[e] = e < E ? row[e] : 0.f;
+        key[e] = order_key(v[e]);
+    }
+    // k <= E (checked by the API); the slots are unrolled so that their
+    // values stay in registers, and k, uniform over the wave, ends them
+    float sel[EMAX];
+    uint32_t taken = 0;
+#pragma unroll
+    for (int j = 0; j < EMAX; ++j) {
+        if (j >= k) continue;
+        int best = 0;
+        uint32_t bk = 0;
+        float bv = 0.f;
+        bool any = false;
+#pragma unroll
+        for (int e = 0; e < EMAX; ++e) {
+            const bool ok = e < E && !((taken >> e) & 1u) && (!any || key[e] > bk);
+            any = any || ok;
+            best = ok ? e : best;
+            bk = ok ? key[e] : bk;
+            bv = ok ? v[e] : bv;
+        }
+        taken |= 1u << best;
+        sel[j] = bv;
+        idx_out[t * k + j] = best;
+    }
+    const float top = sel[0];
+    float z = 0.f;
+    if (gating == kGateTopkSoftmax) {
+#pragma unroll
+        for (int j = 0; j < EMAX; ++j)
+            if (j < k) z += expf(sel[j] - top);
+    } else {
+#pragma unroll
+        for (int e = 0; e < EMAX; ++e)
+            if (e < E) z += expf(v[e] - top);
+    }
+#pragma unroll
+    for (int j = 0; j < EMAX; ++j)
+        if (j < k) w_out[t * k + j] = expf(sel[j] - top) / z;
+}
+template <int EMAX_HI = kLaneGateMax>
+__device__ __forceinline__ void gate_token_lane_any(const float *row, int E, int k, int gating, int64_t t,
+                                           int32_t *__restrict__ idx_out, float *__restrict__ w_out) {
+    if (E <= 8) gate_token_lane<8>(row, E, k, gating, t, idx_out, w_out);
+    else gate_token_lane<EMAX_HI>(row, E, k, gating, t, idx_out, w_out);
+}
+
 // Router GEMM on bf16 MFMA (v_mfma_f32_16x16x32_bf16) + gating epilogue for
 // few experts (16*NT at most; launched for up to 16).  A block owns 16 tokens
 // and its WK waves split the model dimension into WK contiguous ranges.  Each
@@ -87,8 +152,8 @@ __device__ void gate_one_token(const float *row, int E, int k, int gating, int64
 // memory, issuing U chunks of x and of the router weights before their MFMAs
 // so that enough bytes are in flight to stream x at HBM rate (x rows are read
 // once; the router weights stay in L1/L2).  Partial sums meet in LDS in a
-// fixed order, the bias is added, logits are written, and each wave gates
-// whole tokens.
+// fixed order, the bias is added, logits are written, and the first TOK lanes
+// gate one token each.
 __device__ inline float softplus(float u) { return fmaxf(u, 0.f) + log1pf(expf(-fabsf(u))); }
 
 // NOISY adds the noise projection as a second MFMA accumulator set and forms
@@ -203,10 +268,9 @@ __global__ __launch_bounds__(64 * WK) void route_bf16_kernel(
         }
         return;
     }
-    for (int tt = wk; tt < TOK; tt += WK) {
-        const int64_t t = tok0 + tt;
-        if (t < T) gate_one_token(part + tt * LD, E, k, gating, t, idx_out, w_out);
-    }
+    static_assert(EP <= kLaneGateMax, "lane gating covers the block's experts");
+    if (threadIdx.x < TOK && tok0 + threadIdx.x < T)
+        gate_token_lane_any<EP>(part + threadIdx.x * LD, E, k, gating, tok0 + threadIdx.x, idx_out, w_out);
     if constexpr (PERM) {
         extern __shared__ unsigned long long perm_lds[];
         __syncthreads();  // every token's selection is written (and visible to the block)
@@ -243,7 +307,13 @@ __global__ __launch_bounds__(256) void route_f32_kernel(
         }
     }
     __syncthreads();
-    if (live && gating != kGateExpertChoice) gate_one_token(rows[wave], E, k, gating, t, idx_out, w_out);
+    if (gating == kGateExpertChoice) return;
+    if (E <= kLaneGateMax) {
+        const int64_t tl = (int64_t)blockIdx.x * 4 + threadIdx.x;
+        if (threadIdx.x < 4 && tl < T) gate_token_lane_any(rows[threadIdx.x], E, k, gating, tl, idx_out, w_out);
+    } else if (live) {
+        gate_one_token(rows[wave], E, k, gating, t, idx_out, w_out);
+    }
 }
 
 // Logits from the router GEMM's K parts: l[t][e] = sum of the S parts in
@@ -278,7 +348,14 @@ void launch_gate_partials(const float *part, int S, const float *bias, int T, in
                        logits, idx, w);
 }
 
-// Gating alone on given float32 logits [T][E]: one wave per token.
+// Gating alone on given float32 logits [T][E]: one lane per token for up to
+// kLaneGateMax experts, else one wave per token.
+__global__ __launch_bounds__(256) void gate_logits_lane_kernel(const float *__restrict__ logits, int T, int E,
+                                                                int k, int gating, int32_t *__restrict__ idx_out,
+                                                                float *__restrict__ w_out) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t < T) gate_token_lane_any(logits + t * E, E, k, gating, t, idx_out, w_out);
+}
 __global__ __launch_bounds__(256) void gate_logits_kernel(const float *__restrict__ logits, int T, int E,
                                                            int k, int gating, int32_t *__restrict__ idx_out,
                                                            float *__restrict__ w_out) {
@@ -965,7 +1042,11 @@ bool launch_route(const RouteArgs &a, hipStream_t s) {
 void launch_gate_logits(const float *logits, int T, int E, int k, int gating, int32_t *idx, float *w,
                         hipStream_t s) {
     if (T == 0) return;
-    hipLaunchKernelGGL(gate_logits_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, gating, idx, w);
+    if (E <= kLaneGateMax)
+        hipLaunchKernelGGL(gate_logits_lane_kernel, dim3((T + 255) / 256), dim3(256), 0, s, logits, T, E, k, gating,
+                           idx, w);
+    else
+        hipLaunchKernelGGL(gate_logits_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, gating, idx, w);
 }
 
 void launch_ec_select(const float *logits, int T, int E, int C, int32_t *ec_idx, float *ec_score,
