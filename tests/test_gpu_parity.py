@@ -262,10 +262,15 @@ ABI_SPECS = [
 # Tile paths of the 256-row SwiGLU gate/up GEMM: K % 128 == 0 takes the
 # direct-to-LDS kernel, other K the register-staged one; an expert (and a
 # shared expert) of more than 8 m-tiles runs its tiles in bands of 8 m-tiles.
+# Zipf-skewed routing gives the direct-to-LDS kernel tiles of a few rows
+# next to full ones, also in a last round of tiles split along K.
 TILE_SPECS = [
     workloads.MIXTRAL_PREFILL_BF16.replace(name="prefill_tiles_k_not_multiple_of_128", T=1000, d=320, F=384),
     workloads.DEEPSEEK_SHARED_BF16.replace(name="banded_tiles_shared_expert", T=3000, d=256, E=16, k=2, F=64,
                                            F_shared=512),
+    workloads.DEEPSEEK_SHARED_BF16.replace(name="light_tiles_skewed", T=1024, d=512, E=32, k=8, F=256, F_shared=0),
+    workloads.DEEPSEEK_SHARED_BF16.replace(name="light_tiles_split_k", T=1024, d=4096, E=16, k=4, F=128,
+                                           F_shared=0),
 ]
 FFN_SPECS = FFN_SPECS + LONG_K_SPECS + SPLITK_SPECS + ABI_SPECS + TILE_SPECS
 
