@@ -509,8 +509,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
         const float *parts = p.part + (int64_t)wi.unit * wi.S * PER_UNIT;
         const __amdgpu_buffer_rsrc_t prs = buffer_rsrc(parts, (int64_t)wi.S * PER_UNIT * 4);
         const int mine = wi.part * PER_UNIT * 4;  // byte offset of this part's slab
+        // Row blocks past the tile's rows (i >= nact, the same in every part
+        // of the tile) hold zeros and are neither written nor read.
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < TM; ++i) {
+            if (i >= nact) continue;
 #pragma unroll
             for (int j = 0; j < TB; ++j)
 #pragma unroll
@@ -520,27 +523,37 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p) {
                     const int o = (((i * TB + j) * (AR / 4) + q4) * NT + tid) * 16;
                     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), prs, o, mine, kDeviceScope);
                 }
+        }
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's partial stores are complete
         __syncthreads();
         if (tid == 0) last_part = atomicAdd(p.cnt + wi.unit, 1) == wi.S - 1;
         __syncthreads();
         if (!last_part) return;
+        // parts added in part order; this part's own sums come from its
+        // registers (the same values it wrote), so it reads S - 1 slabs
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < TM; ++i) {
+            if (i >= nact) continue;
 #pragma unroll
             for (int j = 0; j < TB; ++j)
 #pragma unroll
                 for (int q4 = 0; q4 < AR / 4; ++q4) {
                     const int o = (((i * TB + j) * (AR / 4) + q4) * NT + tid) * 16;
-                    f32x4 v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(prs, o, 0, kDeviceScope));
-                    for (int sp = 1; sp < wi.S; ++sp)
-                        v += __builtin_bit_cast(
-                            f32x4, __builtin_amdgcn_raw_buffer_load_b128(prs, o, sp * PER_UNIT * 4, kDeviceScope));
+                    const f32x4 own = {acc[i][j][4 * q4], acc[i][j][4 * q4 + 1], acc[i][j][4 * q4 + 2],
+                                       acc[i][j][4 * q4 + 3]};
+                    auto term = [&](int sp) __attribute__((always_inline)) {
+                        return sp == wi.part ? own
+                                             : __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                             prs, o, sp * PER_UNIT * 4, kDeviceScope));
+                    };
+                    f32x4 v = term(0);
+                    for (int sp = 1; sp < wi.S; ++sp) v += term(sp);
                     acc[i][j][4 * q4] = v[0];
                     acc[i][j][4 * q4 + 1] = v[1];
                     acc[i][j][4 * q4 + 2] = v[2];
                     acc[i][j][4 * q4 + 3] = v[3];
                 }
+        }
         if (tid == 0) p.cnt[wi.unit] = 0;  // ready for the next launch
     }
 
