@@ -57,11 +57,11 @@ __device__ inline void store8<float>(float *p, const float *v) {
 // loads of up to kBatch kept rows at once and adds them in slot order, so
 // several loads are in flight per lane.
 constexpr int kBatch = 8;
-template <typename T>
+template <typename T, bool EC>
 __global__ __launch_bounds__(256) void combine_kernel(const T *__restrict__ y_perm, const T *__restrict__ y_shared,
                                                       const float *__restrict__ w,
                                                       const int32_t *__restrict__ slot_row, int Tn, int d, int S,
-                                                      int expert_choice, int parts, T *__restrict__ y) {
+                                                      int parts, T *__restrict__ y) {
     // per-wave tables of the kept rows and gates, S entries each (dynamic
     // LDS sized to S, so that few slots leave room for more waves per CU)
     extern __shared__ int32_t comb_lds[];
@@ -84,7 +84,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const T *__restrict__ y_pe
         if (keep) {
             const int pos = nv + __popcll(m & ((1ull << lane) - 1ull));
             krow[pos] = row;
-            kw[pos] = expert_choice ? w[row] : w[t * S + s];
+            // expert choice: the score sits at the row (w[row]); it is
+            // loaded next to the row's outputs below, so that its latency
+            // does not precede theirs
+            if constexpr (!EC) kw[pos] = w[t * S + s];
         }
         nv += __popcll(m);
     }
@@ -95,13 +98,20 @@ __global__ __launch_bounds__(256) void combine_kernel(const T *__restrict__ y_pe
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         for (int j0 = 0; j0 < nv; j0 += kBatch) {
             float v[kBatch][8];
-#pragma unroll
-            for (int b = 0; b < kBatch; ++b)
-                if (j0 + b < nv) load8<T>(y_perm + (int64_t)krow[j0 + b] * d + c0, v[b]);
+            float gs[EC ? kBatch : 1];
 #pragma unroll
             for (int b = 0; b < kBatch; ++b)
                 if (j0 + b < nv) {
-                    const float g = kw[j0 + b];
+                    const int64_t row = krow[j0 + b];
+                    load8<T>(y_perm + row * d + c0, v[b]);
+                    if constexpr (EC) gs[b] = w[row];
+                }
+#pragma unroll
+            for (int b = 0; b < kBatch; ++b)
+                if (j0 + b < nv) {
+                    float g;
+                    if constexpr (EC) g = gs[b];
+                    else g = kw[j0 + b];
 #pragma unroll
                     for (int i = 0; i < 8; ++i) acc[i] = fmaf(g, v[b][i], acc[i]);
                 }
@@ -125,14 +135,17 @@ void launch_combine(const CombineArgs &a, hipStream_t s) {
     const int parts = (int)std::max<int64_t>(1, std::min<int64_t>(want, a.d / (kWave * 8)));
     const dim3 grid((unsigned)((a.T * parts + 3) / 4));
     const size_t lds = (size_t)4 * a.S * (sizeof(int32_t) + sizeof(float));
-    if (a.bf16)
-        hipLaunchKernelGGL(combine_kernel<bf16>, grid, dim3(256), lds, s, (const bf16 *)a.y_perm,
-                           (const bf16 *)a.y_shared, a.w, a.slot_row, a.T, a.d, a.S, (int)a.expert_choice, parts,
-                           (bf16 *)a.y);
-    else
-        hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), lds, s, (const float *)a.y_perm,
-                           (const float *)a.y_shared, a.w, a.slot_row, a.T, a.d, a.S, (int)a.expert_choice, parts,
-                           (float *)a.y);
+    auto go = [&](auto ec) {
+        constexpr bool EC = decltype(ec)::value;
+        if (a.bf16)
+            hipLaunchKernelGGL((combine_kernel<bf16, EC>), grid, dim3(256), lds, s, (const bf16 *)a.y_perm,
+                               (const bf16 *)a.y_shared, a.w, a.slot_row, a.T, a.d, a.S, parts, (bf16 *)a.y);
+        else
+            hipLaunchKernelGGL((combine_kernel<float, EC>), grid, dim3(256), lds, s, (const float *)a.y_perm,
+                               (const float *)a.y_shared, a.w, a.slot_row, a.T, a.d, a.S, parts, (float *)a.y);
+    };
+    if (a.expert_choice) go(std::true_type{});
+    else go(std::false_type{});
 }
 
 }  // namespace moe

@@ -32,25 +32,29 @@ __device__ void permute_small_block(const int32_t *__restrict__ idx, int T, int 
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     for (int i = tid; i < nc * ES; i += NTH) masks[i] = 0ull;
     __syncthreads();
-    // chunk masks: bit l of masks[c][e] = token 64c + l chose e.  Wave w
-    // takes chunks w, w + NW, ...; each lane issues up to kLoads of its
-    // (chunk, slot) idx loads before the first atomic, so the phase waits
-    // for about one load latency instead of one per chunk.
+    // chunk masks: bit l of masks[c][e] = token 64c + l chose e.  Thread
+    // tid takes slots tid + u * NTH, kLoads idx loads in flight before the
+    // first atomic; its first kLoads slots stay in registers for the
+    // scatter below, which then loads nothing again when the batch has at
+    // most kLoads * NTH slots.
     constexpr int NW = NTH / kWave, kLoads = 8;
     const int n = T * k;  // <= kSmallMaxSlots
-    const int npairs = (nc > wave ? (nc - wave + NW - 1) / NW : 0) * k;
-    for (int p0 = 0; p0 < npairs; p0 += kLoads) {
+    int first_ev[kLoads];
+    for (int i0 = tid; i0 < n; i0 += kLoads * NTH) {
         int ev[kLoads];
 #pragma unroll
         for (int u = 0; u < kLoads; ++u) {
-            const int p = p0 + u, q = p / k, j = p - q * k;
-            const int t = (wave + q * NW) * kChunk + lane;
-            ev[u] = p < npairs && t < T ? idx[t * k + j] : -1;
+            const int i = i0 + u * NTH;
+            ev[u] = i < n ? idx[i] : -1;
         }
 #pragma unroll
         for (int u = 0; u < kLoads; ++u) {
-            const int c = wave + ((p0 + u) / k) * NW, e = ev[u];
-            if (e >= 0 && e < E) atomicOr(&masks[c * ES + e], 1ull << lane);
+            const int i = i0 + u * NTH, e = ev[u];
+            if (e >= 0 && e < E) {
+                const int t = i / k;
+                atomicOr(&masks[(t / kChunk) * ES + e], 1ull << (t % kChunk));
+            }
+            if (i0 == tid) first_ev[u] = e;
         }
     }
     __syncthreads();
@@ -117,13 +121,13 @@ __device__ void permute_small_block(const int32_t *__restrict__ idx, int T, int 
     }
     __syncthreads();
     // rows: offsets[e] + base + rank inside the chunk, or -1 past the capacity
-    // (kLoads idx loads in flight per thread, as above)
+    // (the same slots per thread as above: the first kLoads from registers)
     for (int i0 = tid; i0 < n; i0 += kLoads * NTH) {
         int ev[kLoads];
 #pragma unroll
         for (int u = 0; u < kLoads; ++u) {
             const int i = i0 + u * NTH;
-            ev[u] = i < n ? idx[i] : -1;
+            ev[u] = i0 == tid ? first_ev[u] : (i < n ? idx[i] : -1);
         }
 #pragma unroll
         for (int u = 0; u < kLoads; ++u) {
