@@ -619,11 +619,13 @@ __device__ __forceinline__ void buffer_load16_lds(__amdgpu_buffer_rsrc_t r, bf16
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)dst, 16, voff, soff, 0, 0);
 }
 
-// Gate/up GEMM of the 256-row tiles with its operands loaded from global
-// memory straight into LDS (buffer_load_dwordx4 ... lds), so that no
-// registers stage them: the register-staged kernel above spends 64 VGPRs a
-// thread on its two load sets.  8 waves (2 per SIMD) in 2 (rows) x 4
-// (columns); each wave 128 rows x (32 gate + 32 up) columns on
+// GEMMs of the 256-row tiles with their operands loaded from global memory
+// straight into LDS (buffer_load_dwordx4 ... lds), so that no registers
+// stage them: the register-staged kernel above spends 64 VGPRs a thread on
+// its two load sets.  GLU: the SwiGLU gate/up GEMM, each tile 128 outputs
+// of gate and of up; else the plain down projection (no bias, no
+// activation), each tile 256 outputs.  8 waves (2 per SIMD) in 2 (rows) x 4
+// (columns); each wave 128 rows x 64 B rows (32 gate + 32 up, or 64) on
 // v_mfma_f32_16x16x32_bf16, with the fragments double-buffered.  Waves w and
 // w + 4, which share a SIMD, take different row halves, and in a tile of
 // fewer than BM rows each wave runs only its row blocks that hold rows (as
@@ -646,21 +648,23 @@ __device__ __forceinline__ void buffer_load16_lds(__amdgpu_buffer_rsrc_t r, bf16
 // Alternating launches against the register-staged kernel: Mixtral-shape
 // gate/up 1703 -> 1606 us, DeepSeek-style shared experts 392 -> 341 us,
 // DeepSeek-style routed gate/up unchanged (4391 -> 4435 us).  Fragment reads
-// 2 or 4 per group instead of 3: 1% and 4% slower.  The same schedule on the
-// down projection gained nothing (880 -> 888 us), so that one stays
-// register-staged.
-template <int BM, int BN>
-__global__ __launch_bounds__(512) void gemm_swiglu_lds_kernel(GemmParams p) {
+// 2 or 4 per group instead of 3: 1% and 4% slower.  The down projection on
+// this schedule first gained nothing (880 -> 888 us); with the wave priority
+// of the post-barrier batch (below) it runs 928 -> 858 us.
+template <int BM, int BN, bool GLU>
+__global__ __launch_bounds__(512) void gemm_lds_kernel(GemmParams p) {
     constexpr int WM = 2, WN = 4, NT = 64 * WM * WN, NW = WM * WN;
-    constexpr int BK = 64, NB = 2 * BN;  // B rows of a tile: BN gate rows, then BN up rows
+    // B rows of a tile: BN gate rows, then BN up rows (GLU), or BN rows
+    constexpr int BK = 64, NB = GLU ? 2 * BN : BN;
     constexpr int WTM = BM / WM, WTB = NB / WN;
     constexpr int MF = 16, KSUB = 32;
-    constexpr int TM = WTM / MF, TB = WTB / MF, TN = TB / 2;
+    // TN: output column blocks of a wave
+    constexpr int TM = WTM / MF, TB = WTB / MF, TN = GLU ? TB / 2 : TB;
     constexpr int KCH = BK / 8, RPI = 64 / KCH;          // 16-byte chunks a row; rows a load instruction fills
     constexpr int AI = BM / RPI / NW, BI = NB / RPI / NW;  // load instructions per wave and K tile
     constexpr int RPG = 3;                                 // fragment reads per group
     static_assert(AI >= 1 && BI >= 1 && BK / KSUB == 2, "tile");
-    static_assert(BN % (BI * RPI) == 0, "a wave's B load rows lie in one of gate / up");
+    static_assert(!GLU || BN % (BI * RPI) == 0, "a wave's B load rows lie in one of gate / up");
     // two LDS objects, so that the compiler sees that the fragment reads of
     // one buffer do not alias the direct loads into the other
     __shared__ __attribute__((aligned(16))) bf16 lds0[(BM + NB) * BK];
@@ -689,7 +693,7 @@ __global__ __launch_bounds__(512) void gemm_swiglu_lds_kernel(GemmParams p) {
     const char *abase = p.arow ? (const char *)(p.A + k0) : (const char *)(p.A + tc.row0 * K + k0);
     const __amdgpu_buffer_rsrc_t arsrc =
         buffer_rsrc(abase, p.arow ? p.a_bytes - k0 * 2 : (tc.row_end - tc.row0) * K * 2);
-    const bool bup = wave * BI * RPI >= BN;  // this wave loads up rows (else gate rows)
+    const bool bup = GLU && wave * BI * RPI >= BN;  // this wave loads up rows (else gate rows)
     const bf16 *bmat = bup ? p.B1 : p.B0;
     const __amdgpu_buffer_rsrc_t brsrc =
         buffer_rsrc(bmat + ((int64_t)tc.g * p.N + n0) * K + k0, (int64_t)(p.N - n0) * K * 2);
@@ -708,7 +712,7 @@ __global__ __launch_bounds__(512) void gemm_swiglu_lds_kernel(GemmParams p) {
     for (int i = 0; i < BI; ++i) {
         const int r = (wave * BI + i) * RPI + lrow;  // LDS B row
         const int c = lslot ^ swz_k<BK>(r);
-        boff[i] = (uint32_t)(((int64_t)(r % BN) * K + c * 8) * 2);
+        boff[i] = (uint32_t)(((int64_t)(GLU ? r % BN : r) * K + c * 8) * 2);
     }
     auto load_a = [&](bf16 *L, int i, int ko) __attribute__((always_inline)) {
         buffer_load16_lds(arsrc, L + (wave * AI + i) * RPI * BK, aoff[i], ko);
@@ -728,7 +732,9 @@ __global__ __launch_bounds__(512) void gemm_swiglu_lds_kernel(GemmParams p) {
     const int sw_b = swz_k<BK>(wn * TN * MF + lane % MF);
     const int fa0 = (wm * WTM + lane % MF) * BK;
     const int fb0 = (BM + wn * TN * MF + lane % MF) * BK;
-    auto bofs = [](int j) __attribute__((always_inline)) { return ((j >= TN ? BN : 0) + (j % TN) * MF) * BK; };
+    auto bofs = [](int j) __attribute__((always_inline)) {
+        return GLU ? ((j >= TN ? BN : 0) + (j % TN) * MF) * BK : j * MF * BK;
+    };
 
     f32x4 acc[TM][TB];
 #pragma unroll
@@ -860,7 +866,7 @@ __global__ __launch_bounds__(512) void gemm_swiglu_lds_kernel(GemmParams p) {
     // pairs traded between lanes l and l^1, the tile staged in LDS (rows
     // 0 .. BM/2-1 in lds0, the rest in lds1) for 16-byte row stores.
     static_assert(BM / 2 * BN * 2 <= (int)sizeof(lds0), "half the output tile fits in a staging buffer");
-    constexpr int CPR = BN / 8;
+    constexpr int CPR = BN / 8;  // BN output columns either way
     auto Ct = [&](int r) __attribute__((always_inline)) { return r < BM / 2 ? lds0 + r * BN : lds1 + (r - BM / 2) * BN; };
     const bool odd = lane & 1;
     auto swap1 = [](float x) {
@@ -874,7 +880,10 @@ __global__ __launch_bounds__(512) void gemm_swiglu_lds_kernel(GemmParams p) {
             const int cl = wn * TN * MF + j * MF + lane % MF;
             float v[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) v[r] = silu_fast(acc[i][j][r]) * acc[i][TN + j][r];
+            for (int r = 0; r < 4; ++r) {
+                if constexpr (GLU) v[r] = silu_fast(acc[i][j][r]) * acc[i][TN + j][r];
+                else v[r] = acc[i][j][r];
+            }
             const float xs = swap1(odd ? v[0] : v[2]), ys = swap1(odd ? v[1] : v[3]);
             const int rb = wm * WTM + i * MF + 4 * (lane / 16);
             const int ra0 = rb + (odd ? 2 : 0), ra1 = ra0 + 1;
@@ -1131,18 +1140,21 @@ static void launch_bf16_t(const GemmArgs &a, hipStream_t s, float *partout = nul
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * WM * WN), 0, s, p);
 }
 
-// SwiGLU gate/up on 256-row tiles with direct-to-LDS loads (K % 128 == 0)
-static void launch_swiglu_lds(const GemmArgs &a, hipStream_t s) {
-    constexpr int BM = 256, BN = 128;
-    static_assert((int64_t)BM * 2 * BN <= kSplitUnitFloats, "split-K unit");
-    auto kern = gemm_swiglu_lds_kernel<BM, BN>;
+// 256-row tiles with direct-to-LDS loads (K % 128 == 0): the SwiGLU
+// gate/up GEMM (128 outputs of gate and up) or the plain down projection
+// (256 outputs)
+template <int BN, bool GLU>
+static void launch_lds(const GemmArgs &a, hipStream_t s) {
+    constexpr int BM = 256, NB = GLU ? 2 * BN : BN;
+    static_assert((int64_t)BM * NB <= kSplitUnitFloats, "split-K unit");
+    auto kern = gemm_lds_kernel<BM, BN, GLU>;
     GemmParams p{(const bf16 *)a.A, (const bf16 *)a.B0, (const bf16 *)a.B1, nullptr, (bf16 *)a.C,
                  a.offsets, a.mstart, a.mtile, a.max_mt, a.G, a.rows, a.N, a.K, a.act, nullptr, nullptr, 0, 1, 0,
                  a.arow, a.a_rows * a.K * 2, 0, nullptr, 0};
     int64_t grid = grid_for(a, BM, BN);
     if (grid == 0) return;
     static std::atomic<int> per_cu_cache{-1};
-    grid += split_k_setup(a, kern, 512, BM, 2 * BN, 64, per_cu_cache, p);
+    grid += split_k_setup(a, kern, 512, BM, NB, 64, per_cu_cache, p);
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(512), 0, s, p);
 }
 
@@ -1240,8 +1252,9 @@ void launch_grouped_gemm(const GemmArgs &a, int shape, hipStream_t s) {
         if (glu) launch_bf16_t<128, 128, 2, 4, true, 32, true, 1>(a, s);
         else launch_bf16_t<128, 256, 2, 4, false, 32, true, 1>(a, s);
     } else {
-        if (glu && a.K % 128 == 0) launch_swiglu_lds(a, s);
+        if (glu && a.K % 128 == 0) launch_lds<128, true>(a, s);
         else if (glu) launch_bf16_t<256, 128, 2, 4, true, 16, true, 1, 64, true>(a, s);
+        else if (a.K % 128 == 0 && a.bias == nullptr && a.act == kActNone) launch_lds<256, false>(a, s);
         else launch_bf16_t<256, 256, 2, 4, false, 16, true, 1>(a, s);
     }
 }
