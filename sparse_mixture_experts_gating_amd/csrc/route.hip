@@ -145,6 +145,62 @@ __device__ __forceinline__ void gate_token_lane_any(const float *row, int E, int
     else gate_token_lane<EMAX_HI>(row, E, k, gating, t, idx_out, w_out);
 }
 
+// EG lanes (EG = 8 or 16) gate one token of E <= EG experts whose logits are
+// at `row` (LDS), with the selection and weights of gate_token_lane.  Lane
+// e takes its expert's slot as the number of experts ranked above it (a
+// larger order_key, or an equal key at a lower index), so each lane runs a
+// few dozen independent instructions where one lane per token runs k
+// dependent passes over all experts (about 2 us at the end of every router
+// block).  The largest logit is the rank-0 expert's value; the softmax sums
+// run in slot order (topk-softmax: the selected logits pass through `sel`,
+// EG floats of LDS per token) or expert order (softmax-topk, switch),
+// exactly as in gate_token_lane.  `live` is false for the padding tokens
+// of a ragged last block (they write nothing).
+template <int EG>
+__device__ __forceinline__ void gate_token_group(const float *row, float *sel, int E, int k, int gating,
+                                                 bool live, int64_t t, int32_t *__restrict__ idx_out,
+                                                 float *__restrict__ w_out) {
+    const int e = threadIdx.x % EG;
+    float v[EG];
+    uint32_t key[EG];
+#pragma unroll
+    for (int j = 0; j < EG; ++j) {
+        v[j] = j < E ? row[j] : 0.f;
+        key[j] = order_key(v[j]);
+    }
+    const float mine = e < E ? row[e] : 0.f;
+    const uint32_t kmine = order_key(mine);
+    int rank = 0;
+    uint32_t mk = 0;
+#pragma unroll
+    for (int j = 0; j < EG; ++j)
+        if (j < E) {
+            rank += (key[j] > kmine || (key[j] == kmine && j < e)) ? 1 : 0;
+            mk = key[j] > mk ? key[j] : mk;
+        }
+    float top = 0.f;
+#pragma unroll
+    for (int j = EG - 1; j >= 0; --j)
+        if (j < E && key[j] == mk) top = v[j];  // the lowest index among equal maxima
+    const bool chosen = e < E && rank < k;
+    float z = 0.f;
+    if (gating == kGateTopkSoftmax) {
+        if (chosen) sel[rank] = mine;
+        __builtin_amdgcn_wave_barrier();  // the slot values are written before they are read back
+#pragma unroll
+        for (int j = 0; j < EG; ++j)
+            if (j < k) z += expf(sel[j] - top);
+    } else {
+#pragma unroll
+        for (int j = 0; j < EG; ++j)
+            if (j < E) z += expf(v[j] - top);
+    }
+    if (live && chosen) {
+        idx_out[t * k + rank] = e;
+        w_out[t * k + rank] = expf(mine - top) / z;
+    }
+}
+
 // Router GEMM on bf16 MFMA (v_mfma_f32_16x16x32_bf16) + gating epilogue for
 // few experts (16*NT at most; launched for up to 16).  A block owns 16 tokens
 // and its WK waves split the model dimension into WK contiguous ranges.  Each
@@ -161,7 +217,17 @@ __device__ inline float softplus(float u) { return fmaxf(u, 0.f) + log1pf(expf(-
 // PERM (a batch of one block, T <= 16): the block then permutes its own
 // selections (permute_small_block) and writes the tile plan, which saves
 // the permutation launch of a decode step.
-template <int NT, int WK, bool NOISY, bool PERM = false>
+// PAIR (at most 8 experts, d % 64 == 0, no noise): each 64-wide k step is
+// cut into two 32-wide segments that share one MFMA.  Row r of the A operand
+// is token r % 8 of an 8-token group over segment r / 8, column c of B is
+// expert c % 8 over segment c / 8, so the two diagonal 8 x 8 blocks of the
+// product hold the two segments' partial sums and the others are discarded.
+// One load instruction then covers 128 contiguous bytes of each of 8 token
+// rows (whole cache lines, where the layout above reads half lines of 16
+// rows), both token groups of a block share each B load, and no B lane
+// loads a duplicate expert row.  Prefill router of the Mixtral-shape layer
+// (4096 tokens, d = 4096, bare kernels): 11.0 -> 10.0 us.
+template <int NT, int WK, bool NOISY, bool PERM = false, bool PAIR = false>
 __global__ __launch_bounds__(64 * WK) void route_bf16_kernel(
     const bf16 *__restrict__ x, const bf16 *__restrict__ wg, const float *__restrict__ bias,
     int T, int d, int E, int k, int gating, float *__restrict__ logits,
@@ -193,54 +259,108 @@ __global__ __launch_bounds__(64 * WK) void route_bf16_kernel(
         acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
         if constexpr (NOISY) accn[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    const int nk = d / 32;
-    const int kb = nk * wk / WK, ke = nk * (wk + 1) / WK;
-    auto step = [&](const bf16x8 &a, const bf16x8 *b, const bf16x8 *bn) {
+    if constexpr (PAIR) {
+        static_assert(NT == 1 && !NOISY, "paired segments: up to 8 experts, no noise projection");
+        constexpr int UP = 4;  // 64-wide steps in flight per wave
+        const int seg = r / 8;
+        const bf16 *xp[2];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[nt], acc[nt], 0, 0, 0);
-            if constexpr (NOISY) accn[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bn[nt], accn[nt], 0, 0, 0);
+        for (int g = 0; g < 2; ++g) {
+            int64_t t = tok0 + 8 * g + r % 8;
+            if (t >= T) t = T - 1;
+            xp[g] = x + t * d + seg * 32 + kq;
         }
-    };
-    int kc = kb;
-    for (; kc + U <= ke; kc += U) {
-        bf16x8 a[U], b[U][NT], bn[U][NOISY ? NT : 1];
+        int e = r % 8;
+        if (e >= E) e = E - 1;
+        const bf16 *wp = wg + (int64_t)e * d + seg * 32 + kq;
+        f32x4 pacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+        const int n64 = d / 64;
+        const int kb = n64 * wk / WK, ke = n64 * (wk + 1) / WK;
+        for (int kc = kb; kc < ke; kc += UP) {
+            bf16x8 a[UP][2], b[UP];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            a[u] = __builtin_bit_cast(bf16x8, load16(xa + (kc + u) * 32));
+            for (int u = 0; u < UP; ++u) {
+                // steps past this wave's range re-read its last step (unused)
+                const int ko = min(kc + u, ke - 1) * 64;
+#pragma unroll
+                for (int g = 0; g < 2; ++g) a[u][g] = __builtin_bit_cast(bf16x8, load16(xp[g] + ko));
+                b[u] = __builtin_bit_cast(bf16x8, load16(wp + ko));
+            }
+#pragma unroll
+            for (int u = 0; u < UP; ++u)
+                if (kc + u < ke)
+#pragma unroll
+                    for (int g = 0; g < 2; ++g)
+                        pacc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][g], b[u], pacc[g], 0, 0, 0);
+        }
+        // D[row 4*(lane/16) + j][col r]: the diagonal blocks (row / 8 ==
+        // col / 8) go to the partial table, segment 0 in columns 0..7 and
+        // segment 1 in columns 8..15
+        if (lane / 32 == seg) {
+#pragma unroll
+            for (int g = 0; g < 2; ++g)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    part[(wk * TOK + 8 * g + (4 * (lane / 16) + j) % 8) * LD + r] = pacc[g][j];
+        }
+    } else {
+        const int nk = d / 32;
+        const int kb = nk * wk / WK, ke = nk * (wk + 1) / WK;
+        auto step = [&](const bf16x8 &a, const bf16x8 *b, const bf16x8 *bn) {
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
-                b[u][nt] = __builtin_bit_cast(bf16x8, load16(wg + woff[nt] + (kc + u) * 32));
-                if constexpr (NOISY) bn[u][nt] = __builtin_bit_cast(bf16x8, load16(wn + woff[nt] + (kc + u) * 32));
+                acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[nt], acc[nt], 0, 0, 0);
+                if constexpr (NOISY) accn[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bn[nt], accn[nt], 0, 0, 0);
             }
-        }
+        };
+        int kc = kb;
+        for (; kc + U <= ke; kc += U) {
+            bf16x8 a[U], b[U][NT], bn[U][NOISY ? NT : 1];
 #pragma unroll
-        for (int u = 0; u < U; ++u) step(a[u], b[u], bn[u]);
+            for (int u = 0; u < U; ++u) {
+                a[u] = __builtin_bit_cast(bf16x8, load16(xa + (kc + u) * 32));
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    b[u][nt] = __builtin_bit_cast(bf16x8, load16(wg + woff[nt] + (kc + u) * 32));
+                    if constexpr (NOISY) bn[u][nt] = __builtin_bit_cast(bf16x8, load16(wn + woff[nt] + (kc + u) * 32));
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) step(a[u], b[u], bn[u]);
+        }
+        for (; kc < ke; ++kc) {
+            bf16x8 b[NT], bn[NOISY ? NT : 1];
+            const bf16x8 a = __builtin_bit_cast(bf16x8, load16(xa + kc * 32));
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                b[nt] = __builtin_bit_cast(bf16x8, load16(wg + woff[nt] + kc * 32));
+                if constexpr (NOISY) bn[nt] = __builtin_bit_cast(bf16x8, load16(wn + woff[nt] + kc * 32));
+            }
+            step(a, b, bn);
+        }
+        // D[row = 4*(lane/16) + j][col = lane%16] of each 16x16 tile
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                part[(wk * TOK + 4 * (lane / 16) + j) * LD + nt * 16 + r] = acc[nt][j];
+                if constexpr (NOISY) partn[(wk * TOK + 4 * (lane / 16) + j) * LD + nt * 16 + r] = accn[nt][j];
+            }
     }
-    for (; kc < ke; ++kc) {
-        bf16x8 b[NT], bn[NOISY ? NT : 1];
-        const bf16x8 a = __builtin_bit_cast(bf16x8, load16(xa + kc * 32));
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            b[nt] = __builtin_bit_cast(bf16x8, load16(wg + woff[nt] + kc * 32));
-            if constexpr (NOISY) bn[nt] = __builtin_bit_cast(bf16x8, load16(wn + woff[nt] + kc * 32));
-        }
-        step(a, b, bn);
-    }
-    // D[row = 4*(lane/16) + j][col = lane%16] of each 16x16 tile
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            part[(wk * TOK + 4 * (lane / 16) + j) * LD + nt * 16 + r] = acc[nt][j];
-            if constexpr (NOISY) partn[(wk * TOK + 4 * (lane / 16) + j) * LD + nt * 16 + r] = accn[nt][j];
-        }
     __syncthreads();
     for (int i = threadIdx.x; i < TOK * EP; i += 64 * WK) {
         const int tt = i / EP, e = i % EP;
-        float s = part[tt * LD + e];
+        float s;
+        if constexpr (PAIR) {
+            if (e >= 8) continue;
+            s = part[tt * LD + e] + part[tt * LD + 8 + e];
 #pragma unroll
-        for (int w = 1; w < WK; ++w) s += part[(w * TOK + tt) * LD + e];
+            for (int w = 1; w < WK; ++w) s += part[(w * TOK + tt) * LD + e] + part[(w * TOK + tt) * LD + 8 + e];
+        } else {
+            s = part[tt * LD + e];
+#pragma unroll
+            for (int w = 1; w < WK; ++w) s += part[(w * TOK + tt) * LD + e];
+        }
         if (e < E) {
             if (bias) s += bias[e];
             if constexpr (NOISY) {
@@ -268,9 +388,20 @@ __global__ __launch_bounds__(64 * WK) void route_bf16_kernel(
         }
         return;
     }
-    static_assert(EP <= kLaneGateMax, "lane gating covers the block's experts");
-    if (threadIdx.x < TOK && tok0 + threadIdx.x < T)
-        gate_token_lane_any<EP>(part + threadIdx.x * LD, E, k, gating, tok0 + threadIdx.x, idx_out, w_out);
+    // EG lanes per token (16 tokens x EG <= 256 threads <= the block)
+    static_assert(EP <= 16 && 64 * WK >= TOK * 16, "group gating covers the block's tokens and experts");
+    __shared__ float selv[TOK * 16];
+    if (E <= 8) {
+        if (threadIdx.x < TOK * 8) {
+            const int tt = threadIdx.x / 8;
+            gate_token_group<8>(part + tt * LD, selv + tt * 16, E, k, gating, tok0 + tt < T, tok0 + tt, idx_out,
+                                w_out);
+        }
+    } else if (threadIdx.x < TOK * 16) {
+        const int tt = threadIdx.x / 16;
+        gate_token_group<16>(part + tt * LD, selv + tt * 16, E, k, gating, tok0 + tt < T, tok0 + tt, idx_out,
+                             w_out);
+    }
     if constexpr (PERM) {
         extern __shared__ unsigned long long perm_lds[];
         __syncthreads();  // every token's selection is written (and visible to the block)
@@ -318,8 +449,14 @@ __global__ __launch_bounds__(256) void route_f32_kernel(
 
 // Logits from the router GEMM's K parts: l[t][e] = sum of the S parts in
 // part order, plus the bias, written out and gated from LDS with the same
-// selection and weights as the fused routers.  One wave per token.
-__global__ __launch_bounds__(256) void gate_partials_kernel(const float *__restrict__ part, int S,
+// selection and weights as the fused routers.  One wave per token.  VEC (E a
+// multiple of 4, logits and bias 16-byte aligned): lane l owns experts
+// 4l .. 4l+3, and all S of its 16-byte part loads are issued before any is
+// added (with the parts' loads in one dependent chain, the gating of the
+// DeepSeek-style layer's 8192 tokens took 23 us); the sum runs in the same
+// order either way.
+template <int S, bool VEC>
+__global__ __launch_bounds__(256) void gate_partials_kernel(const float *__restrict__ part,
                                                             const float *__restrict__ bias, int T, int E, int k,
                                                             int gating, float *__restrict__ logits,
                                                             int32_t *__restrict__ idx_out, float *__restrict__ w_out) {
@@ -328,12 +465,31 @@ __global__ __launch_bounds__(256) void gate_partials_kernel(const float *__restr
     const int64_t t = (int64_t)blockIdx.x * 4 + wave;
     if (t >= T) return;
     const int64_t slab = (int64_t)T * E;
-    for (int e = lane; e < E; e += kWave) {
-        float v = part[t * E + e];
-        for (int q = 1; q < S; ++q) v += part[q * slab + t * E + e];
-        if (bias) v += bias[e];
-        rows[wave][e] = v;
-        logits[t * E + e] = v;
+    if constexpr (VEC) {
+        const int e0 = 4 * lane;
+        if (e0 < E) {
+            f32x4 p[S];
+#pragma unroll
+            for (int q = 0; q < S; ++q) p[q] = *(const f32x4 *)(part + q * slab + t * E + e0);
+            f32x4 v = p[0];
+#pragma unroll
+            for (int q = 1; q < S; ++q) v += p[q];
+            if (bias) v += *(const f32x4 *)(bias + e0);
+            *(f32x4 *)(&rows[wave][e0]) = v;
+            *(f32x4 *)(logits + t * E + e0) = v;
+        }
+    } else {
+        for (int e = lane; e < E; e += kWave) {
+            float p[S];
+#pragma unroll
+            for (int q = 0; q < S; ++q) p[q] = part[q * slab + t * E + e];
+            float v = p[0];
+#pragma unroll
+            for (int q = 1; q < S; ++q) v += p[q];
+            if (bias) v += bias[e];
+            rows[wave][e] = v;
+            logits[t * E + e] = v;
+        }
     }
     // gate_one_token reads back the entries each lane wrote; the barrier
     // keeps the compiler from moving those LDS reads above the writes
@@ -341,11 +497,29 @@ __global__ __launch_bounds__(256) void gate_partials_kernel(const float *__restr
     gate_one_token(rows[wave], E, k, gating, t, idx_out, w_out);
 }
 
+template <int S>
+static void launch_gate_partials_s(const float *part, const float *bias, int T, int E, int k, int gating,
+                                   float *logits, int32_t *idx, float *w, hipStream_t s) {
+    const bool vec = (E & 3) == 0 && ((uintptr_t)logits & 15u) == 0 && ((uintptr_t)bias & 15u) == 0 &&
+                     ((uintptr_t)part & 15u) == 0;
+    auto kern = vec ? gate_partials_kernel<S, true> : gate_partials_kernel<S, false>;
+    hipLaunchKernelGGL(kern, dim3((T + 3) / 4), dim3(256), 0, s, part, bias, T, E, k, gating, logits, idx, w);
+}
+
 void launch_gate_partials(const float *part, int S, const float *bias, int T, int E, int k, int gating,
                           float *logits, int32_t *idx, float *w, hipStream_t s) {
     if (T == 0) return;
-    hipLaunchKernelGGL(gate_partials_kernel, dim3((T + 3) / 4), dim3(256), 0, s, part, S, bias, T, E, k, gating,
-                       logits, idx, w);
+    static_assert(kRouterMaxSplit == 8, "one instantiation per part count");
+    switch (S) {
+        case 1: launch_gate_partials_s<1>(part, bias, T, E, k, gating, logits, idx, w, s); break;
+        case 2: launch_gate_partials_s<2>(part, bias, T, E, k, gating, logits, idx, w, s); break;
+        case 3: launch_gate_partials_s<3>(part, bias, T, E, k, gating, logits, idx, w, s); break;
+        case 4: launch_gate_partials_s<4>(part, bias, T, E, k, gating, logits, idx, w, s); break;
+        case 5: launch_gate_partials_s<5>(part, bias, T, E, k, gating, logits, idx, w, s); break;
+        case 6: launch_gate_partials_s<6>(part, bias, T, E, k, gating, logits, idx, w, s); break;
+        case 7: launch_gate_partials_s<7>(part, bias, T, E, k, gating, logits, idx, w, s); break;
+        default: launch_gate_partials_s<8>(part, bias, T, E, k, gating, logits, idx, w, s); break;
+    }
 }
 
 // Gating alone on given float32 logits [T][E]: one lane per token for up to
@@ -986,11 +1160,17 @@ static bool launch_router_tile(const RouteArgs &a, hipStream_t s) {
 template <int NT, int WK>
 static void launch_route_bf16_wk(const RouteArgs &a, const RoutePermuteArgs *perm, hipStream_t s) {
     const int grid = (a.T + 15) / 16;
+    // paired K segments: up to 8 experts, token choice, no noise projection
+    const bool pair = NT == 1 && a.E <= 8 && a.d % 64 == 0 && a.gating != kGateExpertChoice && !a.wn;
     if (perm) {  // one block (route_permute_fits): route, then permute in the same block
         const size_t lds = (size_t)small_tables_bytes(a.T, a.E);
-        hipLaunchKernelGGL((route_bf16_kernel<NT, WK, false, true>), dim3(1), dim3(64 * WK), lds, s,
+        auto kern = pair ? route_bf16_kernel<NT, WK, false, true, NT == 1> : route_bf16_kernel<NT, WK, false, true>;
+        hipLaunchKernelGGL(kern, dim3(1), dim3(64 * WK), lds, s, (const bf16 *)a.x, (const bf16 *)a.wg, a.bias, a.T,
+                           a.d, a.E, a.k, a.gating, a.logits, a.idx, a.w, nullptr, nullptr, *perm, nullptr, nullptr);
+    } else if (pair) {
+        hipLaunchKernelGGL((route_bf16_kernel<NT, WK, false, false, NT == 1>), dim3(grid), dim3(64 * WK), 0, s,
                            (const bf16 *)a.x, (const bf16 *)a.wg, a.bias, a.T, a.d, a.E, a.k, a.gating, a.logits,
-                           a.idx, a.w, nullptr, nullptr, *perm, nullptr, nullptr);
+                           a.idx, a.w, nullptr, nullptr, RoutePermuteArgs{}, nullptr, nullptr);
     } else if (a.wn) {
         hipLaunchKernelGGL((route_bf16_kernel<NT, WK, true>), dim3(grid), dim3(64 * WK), 0, s, (const bf16 *)a.x,
                            (const bf16 *)a.wg, a.bias, a.T, a.d, a.E, a.k, a.gating, a.logits, a.idx, a.w,

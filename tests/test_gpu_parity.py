@@ -103,7 +103,23 @@ ROUTER_DEPTH_SPECS = [
 ]
 
 
-@pytest.mark.parametrize("spec", INT_SPECS + ROUTER_DEPTH_SPECS, ids=lambda s: s.name)
+# Routers of at most 8 experts with d % 64 == 0 pair two 32-wide K segments
+# in one MFMA (the diagonal blocks of the product); waves with no K step
+# (d = 64, 192), uneven K splits (d = 1088, 4160), fewer than 8 experts and
+# ragged token tails.
+PAIR_SPECS = [
+    workloads.MIXTRAL_PREFILL_BF16.replace(name="pair_e8_d64_t37_int", T=37, d=64, F=64, inputs="integer"),
+    workloads.MIXTRAL_PREFILL_BF16.replace(name="pair_e3_d192_t1000_int", T=1000, d=192, E=3, F=64, inputs="integer"),
+    workloads.MIXTRAL_PREFILL_BF16.replace(name="pair_e1_d128_t50_int", T=50, d=128, E=1, k=1, F=64,
+                                           inputs="integer"),
+    workloads.MIXTRAL_PREFILL_BF16.replace(name="pair_e5_k3_d1088_t333_softmax_topk_int", T=333, d=1088, E=5, k=3,
+                                           F=64, gating="softmax_topk", inputs="integer"),
+    workloads.MIXTRAL_PREFILL_BF16.replace(name="pair_e8_d4160_t100_int", T=100, d=4160, F=64, inputs="integer"),
+    workloads.SWITCH_TOP1_BF16.replace(name="pair_switch_e8_d512_int", T=2048, d=512, E=8, F=64, inputs="integer"),
+]
+
+
+@pytest.mark.parametrize("spec", INT_SPECS + ROUTER_DEPTH_SPECS + PAIR_SPECS, ids=lambda s: s.name)
 def test_fused_route_bit_exact_on_exact_inputs(spec):
     inp = workloads.make_inputs(spec, experts=False)
     dinp = to_dev(inp)
