@@ -102,7 +102,7 @@ bool route_permute_fits(int T, int E, bool bf16, bool expert_choice);
 void launch_route_permute(const RouteArgs &a, const RoutePermuteArgs &p, hipStream_t s);
 void launch_permute_small(const PermuteArgs &a, const TilePlanArgs &plan, hipStream_t s);
 void launch_permute_count(const PermuteArgs &a, hipStream_t s);
-void launch_permute_scan(const PermuteArgs &a, hipStream_t s);
+void launch_permute_scan(const PermuteArgs &a, const TilePlanArgs &plan, hipStream_t s);
 void launch_permute_scatter(const PermuteArgs &a, hipStream_t s);
 void launch_ec_permute(const int32_t *ec_idx, int T, int E, int C, int32_t *counts, int32_t *offsets,
                        int32_t *row_token, int32_t *slot_row, hipStream_t s);

@@ -332,8 +332,9 @@ moe_status do_route(const Derived &D, const void *x, const moe_weights *w, const
     return MOE_OK;
 }
 
-// plan non-null: when the one-workgroup permutation runs, it also builds the
-// grouped GEMMs' tile plan and *plan_built is set.
+// plan non-null: the one-workgroup permutation, or else the scan of the
+// three-kernel one, also builds the grouped GEMMs' tile plan, and
+// *plan_built is set.
 moe_status do_permute(const Derived &D, const void *x, const moe_routing *r, void *x_perm, char *ws,
                       const PermuteWs &pw, hipStream_t s, bool gather = true, const TilePlanArgs *plan = nullptr,
                       bool *plan_built = nullptr) {
@@ -347,15 +348,15 @@ moe_status do_permute(const Derived &D, const void *x, const moe_routing *r, voi
         PermuteArgs a{r->topk_idx, (int)D.T, (int)D.E, (int)D.k, D.capacity, D.group_chunks,
                       (int32_t *)(ws + pw.counts), (int32_t *)(ws + pw.pre), (int32_t *)(ws + pw.base),
                       (int32_t *)(ws + pw.ranks), r->counts, r->offsets, r->row_token, r->slot_row};
+        const TilePlanArgs none{0, nullptr, nullptr, 0, nullptr, 0, false};
         if (permute_small_fits((int)D.T, (int)D.E, (int)D.k)) {
-            const TilePlanArgs none{0, nullptr, nullptr, 0, nullptr, 0, false};
             TRY(launch(K_PERM_SMALL, s, [&] { launch_permute_small(a, plan ? *plan : none, s); }));
-            if (plan && plan_built) *plan_built = true;
         } else {
             TRY(launch(K_PERM_COUNT, s, [&] { launch_permute_count(a, s); }));
-            TRY(launch(K_PERM_SCAN, s, [&] { launch_permute_scan(a, s); }));
+            TRY(launch(K_PERM_SCAN, s, [&] { launch_permute_scan(a, plan ? *plan : none, s); }));
             TRY(launch(K_PERM_SCATTER, s, [&] { launch_permute_scatter(a, s); }));
         }
+        if (plan && plan_built) *plan_built = true;
     }
     if (gather)
         TRY(launch(K_GATHER, s, [&] {

@@ -58,8 +58,10 @@ __global__ __launch_bounds__(kScanThreads) void permute_scan_kernel(int nc, int 
                                                                     int32_t *__restrict__ chunk_pre,
                                                                     int32_t *__restrict__ chunk_base,
                                                                     int32_t *__restrict__ counts,
-                                                                    int32_t *__restrict__ offsets) {
+                                                                    int32_t *__restrict__ offsets,
+                                                                    TilePlanArgs plan) {
     __shared__ int wsum[kScanThreads / kWave];
+    __shared__ int lcnt[kScanThreads], loff[kScanThreads + 1];
     const int e = threadIdx.x;
     int kept_total = 0;
     if (e < E) {
@@ -110,8 +112,23 @@ __global__ __launch_bounds__(kScanThreads) void permute_scan_kernel(int nc, int 
         if (w < wave) base += wsum[w];
         total += wsum[w];
     }
-    if (e < E) offsets[e] = base + incl - kept_total;
-    if (e == 0) offsets[E] = total;
+    if (e < E) {
+        offsets[e] = base + incl - kept_total;
+        lcnt[e] = kept_total;
+        loff[e] = base + incl - kept_total;
+    }
+    if (e == 0) {
+        offsets[E] = total;
+        loff[E] = total;
+    }
+    // the grouped GEMMs' tile plan from the counts and offsets in LDS (one
+    // launch fewer than the separate plan kernel: DeepSeek-style layer)
+    if (plan.mstart != nullptr) {
+        __shared__ int plan_scratch[3 * (kMaxPlanExperts + 1)];
+        __syncthreads();
+        build_tile_plan(lcnt, loff, E, plan.BM, plan.mstart, plan.mtile, plan.max_mt, plan.cnt, plan.ncnt,
+                        plan.interleave, plan_scratch);
+    }
 }
 
 __global__ __launch_bounds__(256) void permute_scatter_kernel(const int32_t *__restrict__ idx, int T, int E, int k,
@@ -178,10 +195,10 @@ void launch_permute_count(const PermuteArgs &a, hipStream_t s) {
                        a.k, a.chunk_counts, a.ranks);
 }
 
-void launch_permute_scan(const PermuteArgs &a, hipStream_t s) {
+void launch_permute_scan(const PermuteArgs &a, const TilePlanArgs &plan, hipStream_t s) {
     const int nc = (a.T + kChunk - 1) / kChunk;
     hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, nc, a.E, a.capacity, a.group_chunks,
-                       a.chunk_counts, a.chunk_pre, a.chunk_base, a.counts, a.offsets);
+                       a.chunk_counts, a.chunk_pre, a.chunk_base, a.counts, a.offsets, plan);
 }
 
 void launch_permute_scatter(const PermuteArgs &a, hipStream_t s) {

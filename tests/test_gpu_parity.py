@@ -287,6 +287,10 @@ TILE_SPECS = [
     workloads.DEEPSEEK_SHARED_BF16.replace(name="light_tiles_skewed", T=1024, d=512, E=32, k=8, F=256, F_shared=0),
     workloads.DEEPSEEK_SHARED_BF16.replace(name="light_tiles_split_k", T=1024, d=4096, E=16, k=4, F=128,
                                            F_shared=0),
+    # T*k > 16384: the three-kernel permutation, whose scan also builds the
+    # tile plan in the forward pass (Zipf-skewed, interleaved light tiles)
+    workloads.DEEPSEEK_SHARED_BF16.replace(name="three_kernel_permutation_plan_in_scan", T=2200, d=256, E=64, k=8,
+                                           F=128, F_shared=256),
 ]
 FFN_SPECS = FFN_SPECS + LONG_K_SPECS + SPLITK_SPECS + ABI_SPECS + TILE_SPECS
 
