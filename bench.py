@@ -296,6 +296,13 @@ def main():
     for v in kern.values():
         if v["unit"] == "GB/s":
             v["frac_of_measured_read"] = round(v["achieved"] / hbm["read_gbps"], 4)
+            if v["mbytes"] >= 1.0:
+                # the same read at this kernel's own size, launch and ramp
+                # included (event-timed like the kernel itself)
+                with torch.cuda.stream(stream):
+                    t_read = size_matched_read_us(torch, dev, stream, int(v["mbytes"] * 1e6))
+                v["size_matched_read_us"] = round(t_read, 3)
+                v["frac_of_size_matched_read"] = round(t_read / v["avg_us"], 4)
 
     cpu = parity = None
     if not args.no_cpu_baseline:
@@ -339,6 +346,27 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def size_matched_read_us(torch, dev, stream, nbytes, reps=20):
+    """Event time (us, median of `reps`) of the read `measured_bandwidth`
+    times (float32 row sums of a [rows][4096] view), over `nbytes` rounded up
+    to whole 16 KiB rows: what a plain read of an HBM-bound kernel's own
+    bytes costs at that size, launch and ramp included."""
+    import numpy as np
+    rows = torch.empty((nbytes + 16383) // 16384, 4096, dtype=torch.float32, device=dev).fill_(1.0)
+    rows.sum(dim=1)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        rows.sum(dim=1)
+        e1.record(stream)
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3)
+    del rows
+    return float(np.median(ts))
 
 
 def measured_bandwidth(torch, dev, stream, mib=1024, reps=5):
