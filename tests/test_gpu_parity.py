@@ -386,6 +386,9 @@ COMBINE_SPECS = workloads.SMALL + [
     workloads.DEEPSEEK_SHARED_BF16.replace(name="combine_split_columns_shared", T=3, d=4096, E=16, k=4),
     workloads.BASIC_TOP2_F32.replace(name="combine_split_columns_f32", T=2, d=1536),
     workloads.EXPERT_CHOICE_BF16.replace(name="combine_split_columns_ec", T=64, d=2048, E=4),
+    # expert choice over many tokens: two column ranges per token, ranges of
+    # 68 chunks (a wave's second pass takes 4 of them)
+    workloads.EXPERT_CHOICE_BF16.replace(name="combine_ec_two_ranges", T=3000, d=1088, E=16),
 ]
 
 
