@@ -460,7 +460,7 @@ __global__ __launch_bounds__(256) void gate_partials_kernel(const float *__restr
                                                             const float *__restrict__ bias, int T, int E, int k,
                                                             int gating, float *__restrict__ logits,
                                                             int32_t *__restrict__ idx_out, float *__restrict__ w_out) {
-    __shared__ float rows[4][256];
+    __shared__ __attribute__((aligned(16))) float rows[4][256];  // 16-byte row stores below
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int64_t t = (int64_t)blockIdx.x * 4 + wave;
     if (t >= T) return;
