@@ -918,6 +918,9 @@ struct GemmParamsF32 {
     int N, K;
     int act;
     int kslice;  // K-sliced B as in GemmParams; 0 = B is [N][K]
+    // gathered A: row r of the grouped operand is row arow[r] of A (null:
+    // rows in place)
+    const int32_t *arow;
 };
 
 constexpr int kF32BM = 32;
@@ -952,7 +955,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParamsF32 p) {
         const int r = (tid + 256 * i) / 16;
         int64_t gr = tc.row0 + r;
         if (gr >= tc.row_end) gr = tc.row_end - 1;
-        arow[i] = p.A + gr * K;
+        arow[i] = p.A + (p.arow ? (int64_t)p.arow[gr] : gr) * K;
         int n = n0 + r;
         if (n >= p.N) n = p.N - 1;
 #pragma unroll
@@ -1161,7 +1164,7 @@ static void launch_lds(const GemmArgs &a, hipStream_t s) {
 template <bool GLU>
 static void launch_f32_t(const GemmArgs &a, hipStream_t s) {
     GemmParamsF32 p{(const float *)a.A, (const float *)a.B0, (const float *)a.B1, a.bias, (float *)a.C,
-                    a.offsets, a.mstart, a.mtile, a.max_mt, a.G, a.rows, a.N, a.K, a.act, a.kslice};
+                    a.offsets, a.mstart, a.mtile, a.max_mt, a.G, a.rows, a.N, a.K, a.act, a.kslice, a.arow};
     const int64_t grid = grid_for(a, kF32BM, 32);
     if (grid == 0) return;
     hipLaunchKernelGGL((gemm_f32_kernel<GLU>), dim3((unsigned)grid), dim3(256), 0, s, p);

@@ -152,9 +152,9 @@ struct GemmArgs {
     int act;                // ActKind; kActSwiglu uses B1
     bool bf16;
     SplitKWs split;         // bf16 only; part null = off
-    // bf16 only: A holds a_rows source rows, and row r of the grouped
-    // operand is A row arow[r] (the routed token rows, gathered by the tile
-    // loads themselves).  Needs a_rows * K * 2 < 2^31.
+    // A holds a_rows source rows, and row r of the grouped operand is A row
+    // arow[r] (the routed token rows, gathered by the tile loads
+    // themselves).  bf16 needs a_rows * K * 2 < 2^31 (one buffer resource).
     const int32_t *arow = nullptr;
     int64_t a_rows = 0;
     // K-sliced B (one group, not SwiGLU): B holds K / kslice matrices

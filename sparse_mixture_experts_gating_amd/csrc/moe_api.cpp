@@ -366,9 +366,10 @@ moe_status do_permute(const Derived &D, const void *x, const moe_routing *r, voi
 }
 
 // The forward pass skips the gather kernel when the first GEMM can load the
-// routed token rows itself: bf16 (the grouped MFMA kernel) and all of x
-// addressable by one buffer resource (32-bit byte offsets below 2^31).
-bool gather_in_gemm(const Derived &D) { return D.bf16 && (int64_t)D.T * D.d * 2 <= 0x7fffffff; }
+// routed token rows itself: float32 (the VALU kernel addresses rows through
+// the row map with 64-bit pointers), or bf16 with all of x addressable by one
+// buffer resource (32-bit byte offsets below 2^31).
+bool gather_in_gemm(const Derived &D) { return !D.bf16 || (int64_t)D.T * D.d * 2 <= 0x7fffffff; }
 
 int pick_shape(const Derived &D) {
     if (D.ec) return D.capacity <= 160 ? kGemmSmallM : kGemmPrefill;
@@ -413,7 +414,8 @@ TilePlanArgs plan_args(const Derived &D, char *ws, const FfnWs &fw) {
 }
 
 // x_perm null: the first GEMM reads the routed rows straight from x through
-// the row map (bf16, x within one buffer resource; see gather_in_gemm).
+// the row map (float32, or bf16 with x within one buffer resource; see
+// gather_in_gemm).
 // plan_built: the permutation already wrote the tile plan (plan_args).
 moe_status do_ffn(const Derived &D, const void *x_perm, const void *x, const moe_routing *r, const moe_weights *w,
                   void *y_perm, void *y_shared, char *ws, const FfnWs &fw, hipStream_t s, bool plan_built = false) {

@@ -111,9 +111,13 @@ def test_forward_with_topk_capacity(spec):
     _check_layer(spec, inp, y, routing, ref)
 
 
-def test_noisy_router_zero_noise_is_exact_on_integer_inputs():
-    spec = workloads.MIXTRAL_PREFILL_BF16.replace(name="noisy_int", T=500, d=256, E=64, k=6, F=64, noisy=True,
-                                                  inputs="integer", router_bias="normal")
+@pytest.mark.parametrize("spec", [
+    workloads.MIXTRAL_PREFILL_BF16.replace(name="noisy_int", T=500, d=256, E=64, k=6, F=64, noisy=True,
+                                           inputs="integer", router_bias="normal"),
+    workloads.BASIC_TOP2_F32.replace(name="noisy_f32_int", T=300, d=128, E=8, k=2, noisy=True, inputs="integer",
+                                     router_bias="normal"),
+], ids=lambda s: s.name)
+def test_noisy_router_zero_noise_is_exact_on_integer_inputs(spec):
     inp = workloads.make_inputs(spec, experts=False)
     inp["noise"] = torch.zeros_like(inp["noise"])
     dinp = to_dev(inp)
@@ -143,10 +147,14 @@ def test_noisy_forward_matches_oracle(spec):
     _check_layer(spec, inp, y, routing, ref)
 
 
-# The forward pass loads the routed token rows inside the first GEMM (bf16);
-# the step entry points gather them into x_perm first.  Same products in the
-# same order: the outputs agree bit for bit.
-GATHER_SPECS = [s for s in workloads.SMALL if s.dtype == "bf16"] + [
+# The forward pass loads the routed token rows inside the first GEMM; the
+# step entry points gather them into x_perm first.  Same products in the
+# same order: the outputs agree bit for bit (bf16 and float32 layers).
+GATHER_SPECS = list(workloads.SMALL) + [
+    workloads.BASIC_TOP2_F32.replace(name="fused_gather_f32_swiglu", T=300, d=128, F=192, act="swiglu",
+                                     expert_bias=False),
+    workloads.DEEPSEEK_SHARED_BF16.replace(name="fused_gather_f32_shared", dtype="f32", T=200, d=128, E=16, k=3,
+                                           F=96, F_shared=64),
     workloads.MIXTRAL_PREFILL_BF16.replace(name="fused_gather_split_k", T=700, d=4096, F=256),
     workloads.MIXTRAL_PREFILL_BF16.replace(name="fused_gather_small_m", T=300, d=2048, F=512),
     workloads.MIXTRAL_DECODE_BF16.replace(name="fused_gather_decode", d=512, F=1024),

@@ -119,7 +119,18 @@ PAIR_SPECS = [
 ]
 
 
-@pytest.mark.parametrize("spec", INT_SPECS + ROUTER_DEPTH_SPECS + PAIR_SPECS, ids=lambda s: s.name)
+# float32 routers: up to 64 experts, lanes split each expert's dot product
+# over S = 64 / (E rounded up to a power of two) chunk sets (E = 1: S = 64;
+# E = 3: S = 16; E = 64: S = 1); more experts, one lane per expert.
+F32_ROUTER_SPECS = [
+    workloads.BASIC_TOP2_F32.replace(name="router_f32_e1_int", T=70, d=64, E=1, k=1, inputs="integer"),
+    workloads.BASIC_TOP2_F32.replace(name="router_f32_e3_d272_int", T=130, d=272, E=3, k=2, inputs="integer"),
+    workloads.BASIC_TOP2_F32.replace(name="router_f32_e64_int", T=99, d=128, E=64, k=4, inputs="integer"),
+    workloads.BASIC_TOP2_F32.replace(name="router_f32_e80_int", T=50, d=96, E=80, k=3, inputs="integer"),
+]
+
+
+@pytest.mark.parametrize("spec", INT_SPECS + ROUTER_DEPTH_SPECS + PAIR_SPECS + F32_ROUTER_SPECS, ids=lambda s: s.name)
 def test_fused_route_bit_exact_on_exact_inputs(spec):
     inp = workloads.make_inputs(spec, experts=False)
     dinp = to_dev(inp)
